@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Every ``pin_*`` function takes an oracle handle and raises AssertionError on
+a mismatch.  The tests below run them on the real oracle;
+``test_oracle_mutants.py`` runs them on builds of oracle.c with planted
+mistakes and requires each mistake to be caught.
+
+Pins used (none of them re-types the oracle's formulas):
+  * brute force: shards cut with torch.chunk and rank blocks built by
+    concatenation (tests/brute.py), on tiny shapes, every rank;
+  * a worked layout derived by hand for the tiny workload;
+  * closed forms and page figures (tests/golden/page_figures.json):
+    S = Psi/N when N divides every dim 0 (1/N per GPU, 12.5% at 8), traffic
+    (N-1)/N*Psi per rank, 420 GB per step for a 70B model at 16 bit;
+  * special cases that reduce to exact arithmetic or a library routine:
+    integer-valued bf16 inputs (int64 sum), N=1 (plain cast), N=2 (torch
+    sum), rank order fixed by a cancellation case, -0.0, subnormals, Inf/NaN;
+  * the recursive-summation error bound against an exact rational sum;
+  * all-gather invariants: AG of the shards is the identity, and RS for
+    every rank followed by AG is the per-element rank-order all-reduce.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TINY = workloads.WORKLOADS["tiny"]
+
+# Small shape sweep: ragged dim 0 around N, several inner sizes, 1-D/2-D/3-D,
+# empty parameters.
+SWEEP = [
+    [(5, 7), (16,), (33, 4)],
+    [(1,), (2, 3)],
+    [(0, 5), (7,), (3, 2, 2)],
+    [(9, 1), (8, 8), (11, 3)],
+    [()],
+    [(13, 7), (1, 1), (4,)],
+]
+
+
+def bits_f32(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def random_bits(shape, rng):
+    """bf16 bit patterns of N(0,1) draws (round to nearest even)."""
+    x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32))
+    return workloads.bf16_bits(x.to(torch.bfloat16)).reshape(shape)
+
+
+def bits_of(vals):
+    return workloads.bf16_bits(torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16))
+
+
+# --------------------------------------------------------------------------
+# geometry
+# --------------------------------------------------------------------------
+def pin_tiny_worked_layout(orc):
+    # Worked by hand from "ceil(d0/N) rows per rank, shards padded to that
+    # many rows, parameters packed in order":
+    #   a [5,7]:  c=2, seg=14, off=0;  rows 2,2,1,0 -> L 14,14,7,0;  src 0,14,28,42
+    #   b [16]:   c=4, seg=4,  off=14; rows 4,4,4,4 -> L 4,4,4,4;    src 0,4,8,12
+    #   c [33,4]: c=9, seg=36, off=18; rows 9,9,9,6 -> L 36,36,36,24; src 0,36,72,108
+    #   S = 54, N*S = 216, Psi = 35+16+132 = 183, padding = 33.
+    g = orc.geometry(TINY.shapes, 4)
+    assert g.c == [2, 4, 9]
+    assert g.seg == [14, 4, 36]
+    assert g.off == [0, 14, 18]
+    assert g.S == 54
+    L = [[g.run(r, i)[1] for r in range(4)] for i in range(3)]
+    src = [[g.run(r, i)[0] for r in range(4)] for i in range(3)]
+    assert L == [[14, 14, 7, 0], [4, 4, 4, 4], [36, 36, 36, 24]]
+    assert src == [[0, 14, 28, 42], [0, 4, 8, 12], [0, 36, 72, 108]]
+    assert 4 * g.S - g.psi == 33
+
+
+def pin_geometry_vs_brute(orc):
+    for shapes in SWEEP:
+        for N in (1, 2, 3, 4, 5, 8):
+            for align in (1, 4):
+                g = orc.geometry(shapes, N, align)
+                pos, S = brute.segment_positions(shapes, N, align)
+                assert g.S == S, (shapes, N, align)
+                assert [p for p, _ in pos] == g.off, (shapes, N, align)
+                assert [n for _, n in pos] == g.seg, (shapes, N, align)
+                for i, s in enumerate(shapes):
+                    t = torch.zeros(s if len(s) else (), dtype=torch.int8)
+                    chunks, c = brute.shard_rows(t, N)
+                    inner = g.inner[i]
+                    for r in range(N):
+                        src, L = g.run(r, i)
+                        assert L == chunks[r].numel(), (shapes, N, r, i)
+                        if L:
+                            # first element of the chunk inside the full tensor
+                            start = sum(chunks[q].numel() for q in range(r))
+                            assert src == start, (shapes, N, r, i)
+                        assert orc.shard_run(N, s, r) == (src, L)
+                    assert g.c[i] * inner == g.seg[i]
+
+
+def pin_layout_bijection(orc):
+    for shapes in SWEEP:
+        for N in (1, 3, 4, 8):
+            g = orc.geometry(shapes, N)
+            where, total = brute.layout_map(shapes, N)
+            assert total == N * g.S
+            # oracle's map: element j of param i -> r*S + off_i + (j - src)
+            seen = set()
+            for i in range(len(shapes)):
+                for r in range(N):
+                    src, L = g.run(r, i)
+                    for k in range(L):
+                        pos = r * g.S + g.off[i] + k
+                        assert where[(i, src + k)] == pos
+                        seen.add(pos)
+            assert len(seen) == g.psi == len(where)
+            assert total - len(seen) == N * g.S - g.psi   # padding count
+
+
+def pin_divisible_closed_form(orc):
+    golden = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+    for name in ("llama3_8b_layer", "llama31_70b_layer", "qwen3_30b_a3b_moe_layer",
+                 "llama31_70b_layer_n64"):
+        w = workloads.WORKLOADS[name]
+        g = orc.geometry(w.shapes, w.world)
+        assert g.S * w.world == w.psi, name
+    w = workloads.WORKLOADS["llama31_70b_layer"]
+    g = orc.geometry(w.shapes, 8)
+    assert g.S / g.psi == golden["per_rank_fraction_at_8"]["value"]
+
+
+# --------------------------------------------------------------------------
+# traffic
+# --------------------------------------------------------------------------
+def pin_traffic(orc):
+    # tiny, by hand: (N-1)*S = 162 padded per rank; real 162,162,141,84.
+    real = [orc.rs_traffic(TINY.shapes, 4, R) for R in range(4)]
+    assert [p for _, p in real] == [162] * 4
+    assert [x for x, _ in real] == [162, 162, 141, 84]
+    for shapes in SWEEP:
+        for N in (1, 2, 5, 8):
+            g = orc.geometry(shapes, N)
+            tot = sum(orc.rs_traffic(shapes, N, R)[0] for R in range(N))
+            assert tot == (N - 1) * g.psi          # mean (N-1)/N * Psi per rank
+            for R in range(N):
+                assert orc.rs_traffic(shapes, N, R)[1] == (N - 1) * g.S
+
+
+def pin_traffic_page_figure(orc):
+    golden = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+    f = golden["fsdp_step_bytes_70b_16bit"]
+    shapes = [(70000, 1000000)]                    # Psi = 7e10
+    N = 1000
+    psi = 70000 * 1000000
+    assert psi == f["psi"]
+    per_rank = [orc.rs_traffic(shapes, N, R)[0] for R in range(N)]
+    mean = sum(per_rank) / N
+    assert sum(per_rank) == (N - 1) * psi
+    # forward all-gather + backward all-gather + reduce-scatter, 2 bytes each
+    step_bytes = 3 * mean * f["bytes_per_elem"]
+    assert abs(step_bytes - f["value"]) / f["value"] < 1.1e-3
+    # all-reduce = reduce-scatter + all-gather: FSDP/DDP = 3/2
+    assert (3 * mean) / (2 * mean) == golden["fsdp_over_ddp"]["value"]
+
+
+# --------------------------------------------------------------------------
+# reduce-scatter arithmetic
+# --------------------------------------------------------------------------
+def _rand_case(shapes, N, seed):
+    rng = np.random.default_rng(seed)
+    return [[random_bits(s if len(s) else (), rng) for s in shapes] for _ in range(N)]
+
+
+def pin_rs_vs_brute(orc):
+    cases = [(TINY.shapes, 4), ([(3, 2, 2), (7,)], 3), ([(9, 1), (11, 3)], 5),
+             ([(1,), (2, 3)], 2), ([(0, 5), (6,)], 4)]
+    for idx, (shapes, N) in enumerate(cases):
+        grads = _rand_case(shapes, N, 100 + idx)
+        for align in (1, 4):
+            for R in range(N):
+                got = orc.rs(shapes, N, R, grads, align=align)
+                want = brute.rs_rank_order(grads, shapes, N, R, align)
+                assert np.array_equal(bits_f32(got), bits_f32(want)), (shapes, N, R, align)
+
+
+def pin_rs_integer_exact(orc):
+    rng = np.random.default_rng(7)
+    shapes = [(13, 3), (8,), (5, 2, 3)]
+    for N in (1, 2, 3, 8, 16):
+        ints = [[rng.integers(-8, 9, size=s) for s in shapes] for _ in range(N)]
+        grads = [[bits_of(a.astype(np.float32).reshape(-1)) for a in rank] for rank in ints]
+        g = orc.geometry(shapes, N)
+        for R in range(N):
+            out = orc.rs(shapes, N, R, grads)
+            for i, s in enumerate(shapes):
+                src, L = g.run(R, i)
+                want = sum(ints[r][i].reshape(-1)[src:src + L].astype(np.int64) for r in range(N))
+                seg = out[g.off[i]:g.off[i] + g.seg[i]]
+                assert np.array_equal(seg[:L].astype(np.int64), want), (N, R, i)
+                assert np.all(bits_f32(seg[L:]) == 0)
+
+
+def pin_rs_n1_is_cast(orc):
+    shapes = [(7, 3), (5,)]
+    grads = _rand_case(shapes, 1, 3)
+    out = orc.rs(shapes, 1, 0, grads)
+    want = torch.cat([torch.from_numpy(g.reshape(-1).astype(np.int16)).view(torch.bfloat16).float()
+                      for g in grads[0]])
+    assert np.array_equal(bits_f32(out), bits_f32(want.numpy()))
+
+
+def pin_rs_n2_is_library_sum(orc):
+    shapes = [(9, 5), (4,), (3, 3)]
+    grads = _rand_case(shapes, 2, 4)
+    g = orc.geometry(shapes, 2)
+    for R in range(2):
+        out = orc.rs(shapes, 2, R, grads)
+        for i in range(len(shapes)):
+            src, L = g.run(R, i)
+            ts = [torch.from_numpy(grads[r][i].reshape(-1)[src:src + L].astype(np.int16))
+                  .view(torch.bfloat16) for r in range(2)]
+            want = torch.stack(ts).float().sum(0).numpy()
+            got = out[g.off[i]:g.off[i] + L]
+            assert np.array_equal(bits_f32(got), bits_f32(want)), (R, i)
+
+
+def pin_rs_rank_order(orc):
+    # ranks hold 2^24, 1, -2^24 at the same position.  In rank order:
+    # fl(2^24 + 1) = 2^24 (tie, round to even), then 2^24 - 2^24 = +0.
+    # Any other order (reverse, pairwise) gives 1.
+    vals = [2.0 ** 24, 1.0, -(2.0 ** 24)]
+    grads = [[bits_of([v])] for v in vals]
+    out = orc.rs([(1,)], 3, 0, grads)
+    assert bits_f32(out)[0] == 0x00000000
+    grads_rev = [[bits_of([v])] for v in reversed(vals)]
+    out_rev = orc.rs([(1,)], 3, 0, grads_rev)
+    assert out_rev[0] == np.float32(1.0)
+
+
+def pin_rs_negative_zero(orc):
+    # All ranks -0.0: the sum starts from rank 0's value, so -0.0 survives.
+    grads = [[np.array([0x8000, 0x8000], np.uint16)] for _ in range(4)]
+    out = orc.rs([(2,)], 4, 0, grads)   # c = 1: rank 0 owns element 0
+    assert bits_f32(out)[0] == 0x80000000
+
+
+def pin_rs_subnormals(orc):
+    # bf16 0x0001 = 2^-133 (subnormal).  Sum of N such values is N*2^-133,
+    # exactly representable in binary32 (subnormal): bits N << 16.
+    for N in (2, 3, 8):
+        grads = [[np.array([0x0001], np.uint16)] for _ in range(N)]
+        out = orc.rs([(1,)], N, 0, grads)
+        assert bits_f32(out)[0] == (N << 16), N
+    # mixed sign subnormals cancel exactly
+    grads = [[np.array([0x0003], np.uint16)], [np.array([0x8001], np.uint16)]]
+    out = orc.rs([(1,)], 2, 0, grads)
+    assert bits_f32(out)[0] == (2 << 16)
+
+
+def pin_rs_special_values(orc):
+    inf, ninf, nan, one = 0x7F80, 0xFF80, 0x7FC0, 0x3F80
+    out = orc.rs([(1,)], 2, 0, [[np.array([inf], np.uint16)], [np.array([one], np.uint16)]])
+    assert np.isposinf(out[0])
+    out = orc.rs([(1,)], 2, 0, [[np.array([inf], np.uint16)], [np.array([ninf], np.uint16)]])
+    assert np.isnan(out[0])
+    out = orc.rs([(1,)], 3, 0, [[np.array([one], np.uint16)], [np.array([nan], np.uint16)],
+                                [np.array([one], np.uint16)]])
+    assert np.isnan(out[0])
+
+
+def pin_rs_error_bound(orc):
+    # |rank-order sum - exact sum| <= (N-1) * 2^-24 * sum_r |g_r|
+    shapes = [(16, 3)]
+    for N in (3, 8):
+        grads = _rand_case(shapes, N, 11 + N)
+        g = orc.geometry(shapes, N)
+        for R in (0, N - 1):
+            out = orc.rs(shapes, N, R, grads)
+            src, L = g.run(R, 0)
+            for k in range(L):
+                col = [int(grads[r][0].reshape(-1)[src + k]) for r in range(N)]
+                exact = brute.exact_sum(col)
+                absum = sum(abs(float(brute.widen(b))) for b in col)
+                err = abs(float(out[k]) - float(exact))
+                assert err <= (N - 1) * 2.0 ** -24 * absum, (N, R, k)
+
+
+def pin_rs_slices_match_full(orc):
+    shapes = [(5, 7), (16,), (33, 4)]
+    grads = _rand_case(shapes, 4, 21)
+    g = orc.geometry(shapes, 4)
+    for R in range(4):
+        slices = [[grads[r][i].reshape(-1)[g.run(R, i)[0]:g.run(R, i)[0] + g.run(R, i)[1]]
+                   for i in range(3)] for r in range(4)]
+        a = orc.rs(shapes, 4, R, grads)
+        b = orc.rs_slices(shapes, 4, R, slices)
+        assert np.array_equal(bits_f32(a), bits_f32(b))
+
+
+# --------------------------------------------------------------------------
+# all-gather placement
+# --------------------------------------------------------------------------
+def pin_ag_inverts_sharding(orc):
+    for shapes in SWEEP:
+        for N in (1, 2, 4, 5):
+            for align in (1, 8):
+                rng = np.random.default_rng(N * 31 + align)
+                full = [rng.integers(1, 65535, size=int(np.prod(s)) if len(s) else 1)
+                        .astype(np.uint16).reshape(s if len(s) else ()) for s in shapes]
+                blocks = [brute.rank_block([torch.from_numpy(f.astype(np.int32)) for f in full],
+                                           N, r, align).numpy().astype(np.uint16)
+                          for r in range(N)]
+                out = orc.ag(shapes, N, blocks, elem_bytes=2, align=align)
+                for i in range(len(shapes)):
+                    assert np.array_equal(out[i], full[i].reshape(-1)), (shapes, N, align, i)
+                # slicing the gathered buffer at rank r gives shard r
+                g = orc.geometry(shapes, N, align)
+                for r in range(N):
+                    for i in range(len(shapes)):
+                        src, L = g.run(r, i)
+                        blk = blocks[r][g.off[i]:g.off[i] + L]
+                        assert np.array_equal(blk, full[i].reshape(-1)[src:src + L])
+
+
+def pin_ag_fp32_and_untouched(orc):
+    shapes = [(5, 7), (16,), (33, 4)]
+    N = 4
+    g = orc.geometry(shapes, N)
+    rng = np.random.default_rng(5)
+    blocks = [rng.integers(0, 2 ** 32 - 1, size=g.S, dtype=np.uint32) for _ in range(N)]
+    # poison the padding: the placement must never read it
+    for r in range(N):
+        for i in range(3):
+            src, L = g.run(r, i)
+            blocks[r][g.off[i] + L:g.off[i] + g.seg[i]] = 0xDEADBEEF
+    out = orc.ag(shapes, N, blocks, elem_bytes=4, fill=0xFFFFFFFF)
+    want = brute.ag_by_concat(blocks, shapes, N)
+    for i in range(3):
+        assert np.array_equal(out[i], want[i].astype(np.uint32))
+        assert not np.any(out[i] == 0xDEADBEEF)
+        assert not np.any(out[i] == 0xFFFFFFFF)   # every element written
+
+
+def pin_rs_then_ag_is_allreduce(orc):
+    shapes = [(5, 7), (16,), (33, 4)]
+    N = 4
+    grads = _rand_case(shapes, N, 77)
+    blocks = [orc.rs(shapes, N, R, grads).view(np.uint32) for R in range(N)]
+    full = orc.ag(shapes, N, blocks, elem_bytes=4)
+    for i, s in enumerate(shapes):
+        n = int(np.prod(s))
+        want = np.zeros(n, np.float32)
+        for j in range(n):
+            acc = brute.widen(int(grads[0][i].reshape(-1)[j]))
+            for r in range(1, N):
+                acc = np.float32(acc + brute.widen(int(grads[r][i].reshape(-1)[j])))
+            want[j] = acc
+        assert np.array_equal(full[i], want.view(np.uint32)), i
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(orc, pin):
+    pin(orc)
+
+
+def test_thread_count_does_not_change_bits(orc):
+    shapes = [(257, 9), (1000,)]
+    grads = _rand_case(shapes, 8, 9)
+    n = orc.threads()
+    try:
+        orc.set_threads(1)
+        a = orc.rs(shapes, 8, 3, grads)
+        orc.set_threads(max(2, n))
+        b = orc.rs(shapes, 8, 3, grads)
+    finally:
+        orc.set_threads(n)
+    assert np.array_equal(bits_f32(a), bits_f32(b))
+
+
+def test_tiny_golden(orc):
+    """Stored tiny-workload inputs and oracle outputs (written by
+    tests/golden/make_golden.py, which calls only the oracle) still hold:
+    guards the input generator and the oracle against silent drift."""
+    gold = json.load(open(os.path.join(GOLDEN, "tiny_expected.json")))
+    grads = workloads.all_grads(TINY)
+    for r in range(TINY.world):
+        for i in range(len(TINY.shapes)):
+            assert workloads.bf16_bits(grads[r][i]).reshape(-1).tolist() == gold["grads"][r][i]
+    gb = [[np.array(x, np.uint16) for x in rank] for rank in gold["grads"]]
+    for R in range(TINY.world):
+        out = orc.rs(TINY.shapes, TINY.world, R, gb)
+        assert bits_f32(out).tolist() == gold["rs"][R]
