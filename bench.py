@@ -1,0 +1,442 @@
+"""Benchmark of the TIDE placement collectives on one MI355X.
+
+One step = one pass of the whole hot path over the Llama-3.1-70B-shaped
+decoder layer with 8 emulated ranks in this GPU's HBM:
+  tide_rs  : rank R's fp32 block of the reduce-scatter of the 8 ranks' bf16
+             per-parameter gradients (R rotates over the ranks, so every
+             step streams gradient slices the previous step did not touch),
+             written into its block of the flat rank-major [8, S] buffer;
+  tide_ag  : the rank-major gathered bf16 buffer placed into the full
+             per-parameter bf16 tensors.
+Inputs are resident in HBM before the timed region starts.
+
+Reported (one JSON line on stdout, progress on stderr):
+  value       effective HBM GB/s of the step: algorithmic bytes of both
+              calls / wall time per step;
+  roofline    the dominant kernel's algorithmic bytes per launch / its mean
+              launch time (HIP events on the launch stream) against the
+              8 TB/s HBM peak, plus counter-measured traffic when a
+              committed counter profile of the current kernel source exists;
+  corun       slowdown of a bf16 8192^3 GEMM on another stream while
+              tide_rs runs (default and small-footprint launch) on the
+              64-rank 70B layer;
+  cpu_baseline the CPU oracle on the same step's inputs (host cores).
+
+Algorithmic bytes (what the method must move; the fp32 pack buffer and the
+copy-out pass it avoids are not counted):
+  tide_rs:  2 * N * sum_i L(R,i)  (bf16 reads)  +  4 * S  (fp32 writes)
+  tide_ag:  2 * Psi (bf16 reads)  +  2 * Psi (bf16 writes)
+"""
+import argparse
+import gc
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import parameter_layout_collectives_amd as tide  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "parameter_layout_collectives_amd", "csrc", "tide_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama31_70b_layer.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def rs_bytes(plan, R):
+    real = sum(plan.real(R, i)[1] for i in range(plan.P))
+    return 2 * plan.world * real + 4 * plan.S
+
+
+def ag_bytes(plan):
+    psi = sum(plan.real(r, i)[1] for r in range(plan.world) for i in range(plan.P))
+    return 2 * psi + 2 * psi
+
+
+def timed_events(n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def copy_ceiling(nbytes=2 << 30, reps=10):
+    """Device-to-device copy of nbytes (read + write) as the measured
+    ceiling next to the 8 TB/s spec."""
+    n = nbytes // 2
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        b.copy_(a)
+    ev = timed_events(reps)
+    for s, e in ev:
+        s.record()
+        b.copy_(a)
+        e.record()
+    torch.cuda.synchronize()
+    t = statistics.median(s.elapsed_time(e) for s, e in ev) * 1e-3
+    del a, b
+    return 2 * nbytes / t / 1e9
+
+
+# ---------------------------------------------------------------------------
+# the step
+# ---------------------------------------------------------------------------
+
+class Step:
+    def __init__(self, w, small=False):
+        self.w = w
+        self.small = small
+        N = w.world
+        log(f"generating {w.name}: {N} ranks x {len(w.shapes)} params on the device")
+        self.grads = workloads.all_grads(w, device="cuda")
+        self.plan = tide.Plan(w.shapes, N)
+        S = self.plan.S
+        self.table = tide.grad_table(self.plan, self.grads)
+        self.blocks = torch.zeros(N, S, dtype=torch.float32, device="cuda")
+        self.gathered = workloads.random_bf16(N * S, seed=4242, sigma=w.sigma, device="cuda")
+        self.params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in w.shapes]
+        self.agt = tide.ag_tables(self.plan, self.gathered, self.params)
+        self.b_rs = rs_bytes(self.plan, 0)
+        self.b_ag = ag_bytes(self.plan)
+        torch.cuda.synchronize()
+
+    def rs(self, R):
+        tide.rs(self.plan, R, self.table, self.blocks[R], small=self.small)
+
+    def ag(self):
+        tide.ag(self.plan, None, None, small=self.small, tables=self.agt)
+
+    def run(self, steps, warmup):
+        N = self.w.world
+        for k in range(warmup):
+            self.rs(k % N)
+            self.ag()
+        ev_rs = timed_events(steps)
+        ev_ag = timed_events(steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            ev_rs[k][0].record()
+            self.rs(k % N)
+            ev_rs[k][1].record()
+            ev_ag[k][0].record()
+            self.ag()
+            ev_ag[k][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t_rs = [s.elapsed_time(e) * 1e-3 for s, e in ev_rs]
+        t_ag = [s.elapsed_time(e) * 1e-3 for s, e in ev_ag]
+        return wall, t_rs, t_ag
+
+
+def kernel_stats(name, nbytes, times):
+    mean = statistics.fmean(times)
+    q = sorted(times)
+    return {
+        "kernel": name,
+        "bytes_per_launch": nbytes,
+        "launches": len(times),
+        "mean_us": mean * 1e6,
+        "median_us": statistics.median(times) * 1e6,
+        "p10_us": q[len(q) // 10] * 1e6,
+        "p90_us": q[(9 * len(q)) // 10] * 1e6,
+        "GBps": nbytes / mean / 1e9,
+        "pct_of_peak": 100.0 * nbytes / mean / 1e9 / HBM_PEAK_GBPS,
+    }
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch from the committed counter profile, if it was
+    taken on the current kernel source (else None)."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if doc.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    k = doc.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# co-run with a bf16 GEMM
+# ---------------------------------------------------------------------------
+
+def corun(w, gemm_shape, gemm_reps=20, modes=(False, True)):
+    M, K, Nn = gemm_shape
+    N = w.world
+    log(f"co-run: generating {w.name} ({N} ranks) and a bf16 {M}x{K}x{Nn} GEMM")
+    grads = workloads.all_grads(w, device="cuda")
+    plan = tide.Plan(w.shapes, N)
+    table = tide.grad_table(plan, grads)
+    out = torch.empty(N, plan.S, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    A = torch.randn(M, K, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    B = torch.randn(K, Nn, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    C = torch.empty(M, Nn, dtype=torch.bfloat16, device="cuda")
+    sa = torch.cuda.Stream()
+    sb = torch.cuda.Stream()
+    b_rs = rs_bytes(plan, 0)
+    torch.cuda.synchronize()
+
+    def gemm_alone():
+        ev = timed_events(gemm_reps)
+        with torch.cuda.stream(sa):
+            for _ in range(5):
+                torch.matmul(A, B, out=C)
+            for s, e in ev:
+                s.record()
+                torch.matmul(A, B, out=C)
+                e.record()
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) for s, e in ev]
+
+    def rs_alone(small, reps=10):
+        ev = timed_events(reps)
+        with torch.cuda.stream(sb):
+            for k in range(3):
+                tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
+            for k, (s, e) in enumerate(ev):
+                s.record()
+                tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
+                e.record()
+        torch.cuda.synchronize()
+        return statistics.median(s.elapsed_time(e) for s, e in ev)
+
+    alone = gemm_alone()
+    t_gemm = statistics.median(alone)
+    res = {"gemm": f"bf16 {M}x{K}x{Nn} torch.matmul", "gemm_alone_ms": t_gemm,
+           "gemm_tflops_alone": 2.0 * M * K * Nn / (t_gemm * 1e-3) / 1e12,
+           "workload": w.name, "world": N}
+    for small in modes:
+        t_rs = rs_alone(small)
+        n_rs = int(1.5 * (gemm_reps + 4) * t_gemm / t_rs) + 4
+        base = torch.cuda.Event(enable_timing=True)
+        rs_start = torch.cuda.Event(enable_timing=True)
+        rs_end = torch.cuda.Event(enable_timing=True)
+        first_done = torch.cuda.Event()
+        ev = timed_events(gemm_reps)
+        torch.cuda.synchronize()
+        base.record()
+        sb.wait_stream(torch.cuda.current_stream())
+        sa.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(sb):
+            rs_start.record()
+            tide.rs(plan, 0, table, out[0], small=small, stream=sb)
+            first_done.record()
+            for k in range(1, n_rs):
+                tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
+            rs_end.record()
+        with torch.cuda.stream(sa):
+            sa.wait_event(first_done)
+            for _ in range(2):
+                torch.matmul(A, B, out=C)
+            for s, e in ev:
+                s.record()
+                torch.matmul(A, B, out=C)
+                e.record()
+        torch.cuda.synchronize()
+        rs_lo = base.elapsed_time(rs_start)
+        rs_hi = base.elapsed_time(rs_end)
+        inside = [s.elapsed_time(e) for s, e in ev
+                  if base.elapsed_time(s) >= rs_lo and base.elapsed_time(e) <= rs_hi]
+        key = "small_footprint" if small else "default"
+        med = statistics.median(inside) if inside else None
+        res[key] = {
+            "tide_rs_alone_us": t_rs * 1e3,
+            "tide_rs_alone_GBps": b_rs / (t_rs * 1e-3) / 1e9,
+            "tide_rs_corun_GBps": n_rs * b_rs / ((rs_hi - rs_lo) * 1e-3) / 1e9,
+            "gemm_corun_ms": med,
+            "gemms_fully_overlapped": len(inside),
+            "gemm_slowdown_pct": None if med is None else 100.0 * (med / t_gemm - 1.0),
+        }
+        log(f"co-run {key}: {res[key]}")
+    del grads, table, out, A, B, C
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the same step
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(step, reps=3):
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.default()
+    w, plan = step.w, step.plan
+    N, S, R = w.world, plan.S, 0
+    log("cpu baseline: copying rank-0 gradient slices and the gathered buffer to the host")
+    slices = []
+    for rank in step.grads:
+        row = []
+        for i, g in enumerate(rank):
+            src, L = plan.real(R, i)
+            row.append(g.reshape(-1)[src:src + L].view(torch.int16).cpu().numpy().view(np.uint16))
+        slices.append(row)
+    host = step.gathered.view(torch.int16).cpu().numpy().view(np.uint16)
+    blocks = [host[r * S:(r + 1) * S] for r in range(N)]
+    t_rs, t_ag = [], []
+    for k in range(reps):
+        t0 = time.perf_counter()
+        orc.rs_slices(w.shapes, N, R, slices)
+        t1 = time.perf_counter()
+        orc.ag(w.shapes, N, blocks, elem_bytes=2)
+        t2 = time.perf_counter()
+        t_rs.append(t1 - t0)
+        t_ag.append(t2 - t1)
+        log(f"cpu baseline rep {k}: rs {t1 - t0:.3f} s, ag {t2 - t1:.3f} s")
+    trs, tag = statistics.median(t_rs), statistics.median(t_ag)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": (step.b_rs + step.b_ag) / (trs + tag) / 1e9,
+        "unit": "GB/s",
+        "cores": orc.threads(),
+        "kind": "oracle",
+        "sample": (f"one full step of {w.name} (tide_rs for rank 0 from host copies of its "
+                   f"{N}x{plan.P} gradient slices + tide_ag of the {N}x{S} gathered buffer), "
+                   f"median of {reps}; host copies not timed"),
+        "rs_s": trs,
+        "ag_s": tag,
+        "cpu_model": cpu,
+    }
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama31_70b_layer")
+    ap.add_argument("--small", action="store_true", help="time the small-footprint launch")
+    ap.add_argument("--corun", default="llama31_70b_layer_n64",
+                    help="workload for the co-run GEMM measurement, or 'none'")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the N emulated ranks of the workload live in that GPU's memory.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no HIP device", file=sys.stderr, flush=True)
+        sys.exit(1)
+    tide.lib()   # fails loudly if the HIP library is missing
+
+    w = workloads.WORKLOADS[args.workload]
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name}, {props.multi_processor_count} CUs")
+
+    step = Step(w, small=args.small)
+    log(f"plan: N={w.world} P={step.plan.P} S={step.plan.S} "
+        f"B_rs={step.b_rs} B_ag={step.b_ag}")
+    wall, t_rs, t_ag = step.run(args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    value = (step.b_rs + step.b_ag) * args.steps / wall / 1e9
+    rs_k = kernel_stats("tide_rs", step.b_rs, t_rs)
+    ag_k = kernel_stats("tide_ag", step.b_ag, t_ag)
+    log(f"step {ms_per_step:.3f} ms, {value:.1f} GB/s; rs {rs_k['GBps']:.1f} GB/s, "
+        f"ag {ag_k['GBps']:.1f} GB/s")
+
+    dom = rs_k if sum(t_rs) >= sum(t_ag) else ag_k
+    traffic = counter_traffic(dom["kernel"])
+    roofline = {
+        "bound": "hbm",
+        "kernel": dom["kernel"],
+        "achieved": dom["GBps"],
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": dom["GBps"] / HBM_PEAK_GBPS,
+        "traffic": traffic,
+        "bytes_per_launch": dom["bytes_per_launch"],
+        "mean_launch_us": dom["mean_us"],
+    }
+
+    copy_gbps = None if args.no_copy else copy_ceiling()
+    if copy_gbps:
+        log(f"copy ceiling {copy_gbps:.1f} GB/s")
+    cpu = None if args.no_cpu else cpu_baseline(step)
+    P, S = step.plan.P, step.plan.S
+    del step
+    gc.collect()
+    torch.cuda.empty_cache()
+    corun_res = None
+    if args.corun != "none":
+        cw = workloads.WORKLOADS[args.corun]
+        corun_res = corun(cw, cw.corun_gemm or (8192, 8192, 8192))
+        gc.collect()
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": "tide_rs/tide_ag effective HBM GB/s + % of peak; co-run GEMM slowdown %",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "world": w.world,
+            "params": P,
+            "psi": w.psi,
+            "shard_numel": S,
+            "grad_dtype": "bf16",
+            "shard_dtype": "f32",
+            "ag_dtype": "bf16",
+            "launch": "small_footprint" if args.small else "default",
+            "parallelism": "1 GPU, emulated ranks in one HBM",
+        },
+        "pct_of_peak": 100.0 * value / HBM_PEAK_GBPS,
+        "pct_of_copy_ceiling": None if not copy_gbps else 100.0 * value / copy_gbps,
+        "copy_ceiling_GBps": copy_gbps,
+        "tide_rs": rs_k,
+        "tide_ag": ag_k,
+        "corun": corun_res,
+        "gemm_slowdown_pct": None if not corun_res else {
+            k: corun_res[k]["gemm_slowdown_pct"] for k in ("default", "small_footprint")
+            if k in corun_res},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * tide.h - C ABI of the TIDE placement collectives on one MI355X (gfx950).
+ *
+ * TIDE keeps FSDP2's per-parameter storage and folds the rank-major layout
+ * into the collective's addressing, so neither a gradient pack copy nor an
+ * all-gather copy-out pass is needed ("FSDP通信终局：TIDE零拷贝集合通信优化",
+ * kongchang.com, §"FSDP2通信开销的根源" and §"TIDE的设计思路：布局感知的零拷贝通信").
+ * This library implements one GPU's share of that hot path, with the N ranks
+ * of a data-parallel group held as N pointer sets in one device's memory:
+ *
+ *   tide_plan_*  dim-0 shard geometry with ceil padding and the offsets of
+ *                every parameter inside a rank block;
+ *   tide_rs      TIDE-RS: per-parameter bf16 gradients of N ranks -> this
+ *                rank's fp32 block of the flat rank-major shard buffer,
+ *                summed in fp32 in rank order (no pack copy);
+ *   tide_ag      TIDE-AG placement: a rank-major gathered buffer -> full
+ *                per-parameter tensors (no copy-out pass).
+ *
+ * Notation.  N = world (ranks), P = nparams.  Parameter i is a row-major
+ * tensor viewed as [dim0_i, inner_i] (inner = product of the trailing dims;
+ * a 0-dim tensor is [1, 1]).  Psi = sum_i dim0_i * inner_i.
+ *   c_i     = ceil(dim0_i / N)              rows of parameter i per rank
+ *   seg_i   = c_i * inner_i                 elements of parameter i per rank block
+ *   off_0   = 0, off_{i+1} = roundup(off_i + seg_i, align)
+ *   S       = roundup(off_{P-1} + seg_{P-1}, align)    elements per rank block
+ *   src(r,i)= r * c_i * inner_i             first element of rank r's shard
+ *   L(r,i)  = min(c_i, max(0, dim0_i - r*c_i)) * inner_i   real elements of it
+ * Rank r's block holds, at off_i + k for k < L(r,i), element src(r,i)+k of
+ * parameter i; positions off_i+L(r,i) .. off_i+seg_i-1 are padding, and the
+ * positions between segments (align > 1) are gaps.  Each rank keeps 1/N of
+ * every parameter (tqpw.cn "FSDP技术演进全景图" §2.1); trailing ranks may hold
+ * fewer rows, or none.
+ *
+ * Ownership and threading.  The caller owns every device buffer and stream.
+ * A plan owns its host geometry and, per device it is used on, small device
+ * tables (parameter descriptors, tile lists and a cache of uploaded pointer
+ * tables).  Host pointer arrays passed to tide_rs / tide_ag are read during
+ * the call only.  A plan may be used from several host threads at once.
+ *
+ * Errors.  Every call returns a tide_status and never aborts.  All argument
+ * checks run before anything is enqueued: on an error nothing is launched
+ * and no output is touched.  tide_last_error() gives a message for the last
+ * non-OK status returned on the calling thread.  A device fault inside a
+ * launched kernel surfaces, as for any HIP launch, at the caller's next
+ * synchronisation.
+ *
+ * Streams.  tide_rs and tide_ag are asynchronous and stream-ordered on the
+ * given hipStream_t (passed as void*; NULL = the null stream).  The first
+ * call of a plan on a device, and a call with a pointer set the plan has not
+ * seen recently, upload small tables with blocking copies before launching.
+ */
+#ifndef TIDE_H
+#define TIDE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tide_status {
+    TIDE_OK = 0,
+    TIDE_E_INVALID = 1,      /* argument out of range, null, misaligned or overlapping */
+    TIDE_E_UNSUPPORTED = 2,  /* well-formed request the library does not implement */
+    TIDE_E_NOMEM = 3,        /* host or device allocation failed */
+    TIDE_E_HIP = 4           /* a HIP runtime call failed; message names it */
+} tide_status;
+
+/* Opaque plan: the shard geometry of one parameter list for one world size. */
+typedef struct tide_plan tide_plan;
+
+/* Launch flag: small-footprint mode.  Caps the number of workgroups so that
+ * a compute kernel on another stream (a bf16 GEMM) keeps most of the chip.
+ * The pages trace interference to collectives that occupy the compute units
+ * a concurrent GEMM needs (TIDE article, §"FSDP2通信开销的根源"), and TIDE's
+ * answer is to keep collectives off them (§"TIDE的设计思路"). */
+#define TIDE_F_SMALL_FOOTPRINT 0x1u
+
+/* ---------------------------------------------------------------------- */
+/* Plan (host only; makes no HIP call).                                    */
+/* ---------------------------------------------------------------------- */
+
+/* Build the geometry above.
+ *   world        N >= 1 ranks (at most 65536).
+ *   nparams      P >= 1 parameters (at most 1<<24).
+ *   dim0, inner  host arrays of P non-negative sizes; dim0*inner and the
+ *                rank block size must fit in int64 (and N*S too).
+ *   align_elems  >= 1: offset granularity inside a rank block (1 = tight).
+ *   out_plan     receives the plan; set to NULL on error.
+ * Returns TIDE_E_INVALID on a bad size, TIDE_E_NOMEM if allocation fails. */
+tide_status tide_plan_create(int32_t world, int32_t nparams, const int64_t *dim0,
+                             const int64_t *inner, int64_t align_elems,
+                             tide_plan **out_plan);
+
+/* Release a plan.  Waits for the devices the plan was used on to go idle
+ * before freeing its device tables.  NULL is ignored. */
+void tide_plan_destroy(tide_plan *plan);
+
+int32_t tide_plan_world(const tide_plan *plan);          /* N, or -1 if plan is NULL */
+int32_t tide_plan_nparams(const tide_plan *plan);        /* P, or -1 */
+int64_t tide_plan_shard_numel(const tide_plan *plan);    /* S, or -1 */
+
+/* Geometry of parameter i: off_i, c_i, seg_i (any output may be NULL). */
+tide_status tide_plan_param(const tide_plan *plan, int32_t i, int64_t *off,
+                            int64_t *rows_per_rank, int64_t *seg_numel);
+
+/* Rank r's shard of parameter i: src(r,i) and L(r,i) (outputs may be NULL). */
+tide_status tide_plan_real(const tide_plan *plan, int32_t rank, int32_t i,
+                           int64_t *src_off, int64_t *real_numel);
+
+/* ---------------------------------------------------------------------- */
+/* TIDE-RS (TIDE article §"TIDE的设计思路"; reduce-scatter semantics from   */
+/* §"FSDP2通信开销的根源" and apxml "Communication volume analysis"         */
+/* §"分片中的通信原语"; fp32 reduction dtype, tqpw.cn blog §3.2).            */
+/* ---------------------------------------------------------------------- */
+
+/* Write rank `rank`'s fp32 block (S floats) of the reduce-scatter:
+ *   out[off_i + k] = sum over r = 0..N-1, in that order, of
+ *                    widen(grads[r*P + i][src(rank,i) + k])   for k < L(rank,i)
+ *   out[off_i + k] = +0.0f for L(rank,i) <= k < seg_i, and gaps are +0.0f.
+ * widen(b) is exact (bf16 bits shifted into the top of an fp32); every add
+ * is one IEEE binary32 round-to-nearest-even addition with subnormals kept,
+ * so the result is bit-for-bit reproducible.
+ *   plan    a plan from tide_plan_create.
+ *   rank    0 <= rank < N.
+ *   grads   host array of N*P device pointers; entry r*P + i is rank r's bf16
+ *           gradient of parameter i, dim0_i*inner_i elements, row-major,
+ *           2-byte aligned.  Only the elements of rank `rank`'s shard are
+ *           read.  Entries with L(rank,i) = 0 may be NULL.
+ *   out     device pointer to S floats (4-byte aligned), e.g. block `rank`
+ *           of an N*S buffer; must not overlap any element that is read.
+ *   flags   0 or TIDE_F_SMALL_FOOTPRINT; other bits -> TIDE_E_UNSUPPORTED.
+ *   max_workgroups  0 = the policy for `flags`; > 0 caps the grid.
+ *   stream  hipStream_t (NULL = null stream).
+ * 16-byte aligned pointers take the vector path; other alignments are
+ * handled element by element with identical results. */
+tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *const *grads,
+                    float *out, uint32_t flags, int32_t max_workgroups, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* TIDE-AG placement (TIDE article §"TIDE的设计思路"; all-gather semantics  */
+/* from apxml "Communication volume analysis" §"分片中的通信原语").          */
+/* ---------------------------------------------------------------------- */
+
+/* Scatter N rank blocks straight into full per-parameter tensors:
+ *   params[i][src(r,i) + k] = rank_src[r][off_i + k]   for every r, i, k < L(r,i)
+ * as an exact copy of elem_bytes-byte elements.  Padding and gaps are never
+ * read; every element of every parameter is written exactly once.
+ *   rank_src    host array of N device pointers, each to a rank block of S
+ *               elements (e.g. base + r*S*elem_bytes of a gathered buffer).
+ *   params      host array of P device pointers to the full tensors
+ *               (dim0_i*inner_i elements; NULL allowed when that is 0).
+ *   elem_bytes  2 (bf16/fp16) or 4 (fp32).
+ *   flags, max_workgroups, stream  as for tide_rs.
+ * Destinations must not overlap one another or any element that is read. */
+tide_status tide_ag(const tide_plan *plan, const void *const *rank_src,
+                    void *const *params, int32_t elem_bytes, uint32_t flags,
+                    int32_t max_workgroups, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Diagnostics.                                                            */
+/* ---------------------------------------------------------------------- */
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char *tide_last_error(void);
+
+/* Fixed name of a status code. */
+const char *tide_status_string(tide_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDE_H */

@@ -1,0 +1,192 @@
+"""Python binding of the TIDE placement collectives (libtide.so).
+
+Argument marshalling only: every step of tide_rs / tide_ag runs in the HIP
+kernels of libtide.so.  PyTorch supplies device memory and streams.
+
+    plan = Plan(shapes, world)                  # tide_plan_create
+    rs(plan, rank, grads, out)                  # tide_rs  (TIDE-RS)
+    ag(plan, rank_src, params)                  # tide_ag  (TIDE-AG placement)
+
+TIDE-RS and TIDE-AG are described in "FSDP通信终局：TIDE零拷贝集合通信优化"
+(kongchang.com), §"TIDE的设计思路：布局感知的零拷贝通信".
+"""
+import ctypes
+
+import torch
+
+from ._lib import lib
+
+SMALL_FOOTPRINT = 0x1
+
+_STATUS = {0: "TIDE_OK", 1: "TIDE_E_INVALID", 2: "TIDE_E_UNSUPPORTED", 3: "TIDE_E_NOMEM",
+           4: "TIDE_E_HIP"}
+
+
+class TideError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != 0:
+        msg = lib().tide_last_error()
+        raise TideError(status, msg.decode() if msg else "")
+
+
+def _rows_inner(shape):
+    shape = tuple(int(s) for s in shape)
+    if not shape:
+        return 1, 1
+    inner = 1
+    for s in shape[1:]:
+        inner *= s
+    return shape[0], inner
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """Shard geometry of a parameter list for `world` ranks (tide_plan)."""
+
+    def __init__(self, shapes, world, align=1):
+        self.shapes = [tuple(int(x) for x in s) for s in shapes]
+        self.world = int(world)
+        P = len(self.shapes)
+        d0 = (ctypes.c_int64 * max(P, 1))(*[_rows_inner(s)[0] for s in self.shapes])
+        inner = (ctypes.c_int64 * max(P, 1))(*[_rows_inner(s)[1] for s in self.shapes])
+        h = ctypes.c_void_p()
+        self._h = None
+        _check(lib().tide_plan_create(self.world, P, d0, inner, int(align), ctypes.byref(h)))
+        self._h = h
+        self.S = int(lib().tide_plan_shard_numel(h))
+        self.P = P
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None:
+            lib().tide_plan_destroy(self._h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def param(self, i):
+        """(off_i, rows per rank c_i, seg_i)."""
+        off, c, seg = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().tide_plan_param(self._h, i, ctypes.byref(off), ctypes.byref(c),
+                                     ctypes.byref(seg)))
+        return off.value, c.value, seg.value
+
+    def real(self, rank, i):
+        """(src, L): rank's shard of param i starts at element src, L real elements."""
+        src, L = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().tide_plan_real(self._h, rank, i, ctypes.byref(src), ctypes.byref(L)))
+        return src.value, L.value
+
+
+class PointerTable:
+    """A host array of device pointers kept alive with the tensors it names.
+    Build it once and pass it to rs/ag repeatedly to skip re-marshalling."""
+
+    def __init__(self, tensors):
+        self.tensors = list(tensors)
+        self.array = (ctypes.c_void_p * max(len(self.tensors), 1))(
+            *[t.data_ptr() if t is not None else None for t in self.tensors])
+
+
+def grad_table(plan, grads):
+    """PointerTable for tide_rs: grads[r][i] = rank r's bf16 gradient of param i."""
+    if len(grads) != plan.world:
+        raise ValueError(f"expected {plan.world} ranks of gradients, got {len(grads)}")
+    flat = []
+    for r, rank in enumerate(grads):
+        if len(rank) != plan.P:
+            raise ValueError(f"rank {r}: expected {plan.P} gradients, got {len(rank)}")
+        for i, t in enumerate(rank):
+            if t.dtype != torch.bfloat16:
+                raise TypeError(f"grads[{r}][{i}] must be bfloat16, got {t.dtype}")
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"grads[{r}][{i}] must be a contiguous device tensor")
+            if t.numel() != _numel(plan.shapes[i]):
+                raise ValueError(f"grads[{r}][{i}] has {t.numel()} elements, "
+                                 f"expected {_numel(plan.shapes[i])}")
+            flat.append(t)
+    return PointerTable(flat)
+
+
+def _numel(shape):
+    n = 1
+    for s in shape:
+        n *= s
+    return n
+
+
+def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None):
+    """TIDE-RS: write rank `rank`'s fp32 block (plan.S floats) into `out`.
+
+    grads: list over ranks of lists over params of bf16 device tensors, or a
+    PointerTable from grad_table().  out: contiguous fp32 device tensor with
+    plan.S elements (e.g. a row of an [N, S] buffer)."""
+    if not isinstance(grads, PointerTable):
+        grads = grad_table(plan, grads)
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 device tensor")
+    if out.numel() != plan.S:
+        raise ValueError(f"out has {out.numel()} elements, expected S = {plan.S}")
+    _check(lib().tide_rs(plan.handle, int(rank), grads.array, ctypes.c_void_p(out.data_ptr()),
+                         SMALL_FOOTPRINT if small else 0, int(max_workgroups),
+                         _stream_handle(stream)))
+
+
+_ELEM = {torch.bfloat16: 2, torch.float16: 2, torch.int16: 2, torch.float32: 4, torch.int32: 4}
+
+
+def ag_tables(plan, rank_src, params):
+    """(PointerTable of rank blocks, PointerTable of params, element bytes)."""
+    if isinstance(rank_src, torch.Tensor):
+        if rank_src.numel() != plan.world * plan.S:
+            raise ValueError(f"gathered buffer has {rank_src.numel()} elements, "
+                             f"expected N*S = {plan.world * plan.S}")
+        if not rank_src.is_contiguous():
+            raise ValueError("gathered buffer must be contiguous")
+        flat = rank_src.reshape(-1)
+        blocks = [flat[r * plan.S:(r + 1) * plan.S] for r in range(plan.world)]
+    else:
+        blocks = list(rank_src)
+    if len(blocks) != plan.world or len(params) != plan.P:
+        raise ValueError("need one block per rank and one tensor per parameter")
+    dt = blocks[0].dtype
+    if dt not in _ELEM:
+        raise TypeError(f"unsupported element type {dt}")
+    for r, b in enumerate(blocks):
+        if b.dtype != dt or not b.is_cuda or not b.is_contiguous() or b.numel() < plan.S:
+            raise ValueError(f"rank block {r} must be a contiguous {dt} device tensor "
+                             f"of at least S elements")
+    for i, t in enumerate(params):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"params[{i}] must be a contiguous {dt} device tensor")
+        if t.numel() != _numel(plan.shapes[i]):
+            raise ValueError(f"params[{i}] has {t.numel()} elements, "
+                             f"expected {_numel(plan.shapes[i])}")
+    return PointerTable(blocks), PointerTable(params), _ELEM[dt]
+
+
+def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, tables=None):
+    """TIDE-AG placement: scatter N rank blocks into full parameter tensors.
+
+    rank_src: one contiguous N*S buffer (rank-major) or a list of N blocks.
+    params: list of P full tensors of the same dtype (2- or 4-byte elements).
+    tables: optional result of ag_tables() to skip re-marshalling."""
+    src_t, dst_t, e = tables if tables is not None else ag_tables(plan, rank_src, params)
+    _check(lib().tide_ag(plan.handle, src_t.array, dst_t.array, e,
+                         SMALL_FOOTPRINT if small else 0, int(max_workgroups),
+                         _stream_handle(stream)))
+
+
+__all__ = ["Plan", "PointerTable", "TideError", "SMALL_FOOTPRINT", "grad_table", "ag_tables",
+           "rs", "ag", "lib"]

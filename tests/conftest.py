@@ -17,6 +17,12 @@ def pytest_configure(config):
     if not os.path.exists(lib):
         from oracle import build_oracle
         build_oracle.build()
+    # The HIP library is built ahead of time (__graft_entry__.build());
+    # build it here only if nothing is built yet.
+    tide_lib = os.path.join(ROOT, "parameter_layout_collectives_amd", "libtide.so")
+    if not os.path.exists(tide_lib):
+        from parameter_layout_collectives_amd import build as tide_build
+        tide_build.build()
 
 
 @pytest.fixture(scope="session")

@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU parity tests: host copies of device data and
+the oracle's expected values for them.  Inputs always come from the seeded
+generators in workloads.py; expected values always come from the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import parameter_layout_collectives_amd as tide
+
+F32_SENTINEL = 0x7FBADBAD      # a NaN pattern no kernel produces
+BF16_SENTINEL = 0x7FBD
+
+
+def note(msg):
+    """Name the case before each GPU step (flushed, so a crash still shows it)."""
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def bits16(t):
+    """Device or host bf16/int16 tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bits32(t):
+    return t.detach().contiguous().view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def rank_slices(plan, grads, R):
+    """slices[r][i] = host copy of the elements of rank r's gradient of param
+    i that fall in rank R's shard (what tide_rs reads)."""
+    out = []
+    for rank in grads:
+        row = []
+        for i, g in enumerate(rank):
+            src, L = plan.real(R, i)
+            row.append(bits16(g.reshape(-1)[src:src + L]))
+        out.append(row)
+    return out
+
+
+def expected_rs(orc, shapes, N, R, grads, plan, align=1):
+    return orc.rs_slices(shapes, N, R, rank_slices(plan, grads, R), align=align)
+
+
+def same_f32(got, want):
+    """Bitwise equality, except that NaNs compare by class only."""
+    g = np.asarray(got, np.float32)
+    w = np.asarray(want, np.float32)
+    gn, wn = np.isnan(g), np.isnan(w)
+    if not np.array_equal(gn, wn):
+        return False
+    return np.array_equal(g[~gn].view(np.uint32), w[~wn].view(np.uint32))
+
+
+def first_mismatch(got, want):
+    g = np.asarray(got, np.float32).view(np.uint32)
+    w = np.asarray(want, np.float32).view(np.uint32)
+    idx = np.nonzero(g != w)[0]
+    if idx.size == 0:
+        return None
+    k = int(idx[0])
+    return k, hex(int(g[k])), hex(int(w[k])), int(idx.size)
+
+
+def run_rs(plan, R, grads_or_table, out, **kw):
+    tide.rs(plan, R, grads_or_table, out, **kw)
+    torch.cuda.synchronize()

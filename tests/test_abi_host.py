@@ -1,0 +1,186 @@
+"""Host-side checks of libtide.so that need no GPU.
+
+* the library loads and exports every function include/tide.h declares;
+* tide_plan_* geometry equals the CPU oracle's on a sweep of shapes
+  (the plan code and the oracle share no code);
+* every argument error returns its status and message before anything is
+  enqueued (these calls never reach the HIP runtime).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import parameter_layout_collectives_amd as tide
+from parameter_layout_collectives_amd._lib import SIGNATURES, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tide.h")
+
+E_INVALID, E_UNSUPPORTED = 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tide_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(SIGNATURES)
+
+
+def test_status_strings():
+    L = lib()
+    assert L.tide_status_string(0) == b"TIDE_OK"
+    assert L.tide_status_string(4) == b"TIDE_E_HIP"
+
+
+SHAPE_SWEEP = [
+    [(5, 7), (16,), (33, 4)],
+    [(0, 5), (7,), (3, 2, 2), ()],
+    [(9, 1), (8, 8), (11, 3)],
+    [(4096, 4096), (1024, 4096), (14336, 4096), (4096,)],
+]
+
+
+@pytest.mark.parametrize("shapes", SHAPE_SWEEP)
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 8, 64])
+@pytest.mark.parametrize("align", [1, 4, 64])
+def test_plan_matches_oracle(orc, shapes, N, align):
+    plan = tide.Plan(shapes, N, align)
+    g = orc.geometry(shapes, N, align)
+    assert plan.S == g.S
+    for i in range(len(shapes)):
+        assert plan.param(i) == (g.off[i], g.c[i], g.seg[i])
+        for r in range(N):
+            assert plan.real(r, i) == g.run(r, i)
+
+
+def _create(world, dims, align=1):
+    P = len(dims)
+    d0 = (ctypes.c_int64 * max(P, 1))(*[d for d, _ in dims])
+    inner = (ctypes.c_int64 * max(P, 1))(*[n for _, n in dims])
+    h = ctypes.c_void_p(1234)
+    st = lib().tide_plan_create(world, P, d0, inner, align, ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("world,dims,align,needle", [
+    (0, [(4, 4)], 1, "world"),
+    (70000, [(4, 4)], 1, "world"),
+    (2, [], 1, "nparams"),
+    (2, [(-1, 4)], 1, "negative"),
+    (2, [(4, -4)], 1, "negative"),
+    (2, [(4, 4)], 0, "align"),
+    (2, [(2 ** 62, 4)], 1, "overflow"),
+    (2, [(2 ** 40, 2 ** 20), (2 ** 40, 2 ** 20)], 1, "overflow"),
+])
+def test_plan_create_errors(world, dims, align, needle):
+    st, h = _create(world, dims, align)
+    assert st == E_INVALID
+    assert h.value is None
+    assert needle in lib().tide_last_error().decode()
+
+
+def test_plan_query_errors():
+    plan = tide.Plan([(4, 4)], 2)
+    x = ctypes.c_int64()
+    L = lib()
+    assert L.tide_plan_param(plan.handle, 1, ctypes.byref(x), None, None) == E_INVALID
+    assert L.tide_plan_param(plan.handle, -1, None, None, None) == E_INVALID
+    assert L.tide_plan_real(plan.handle, 2, 0, None, None) == E_INVALID
+    assert L.tide_plan_real(None, 0, 0, None, None) == E_INVALID
+    assert L.tide_plan_shard_numel(None) == -1
+    assert L.tide_plan_world(plan.handle) == 2
+    assert L.tide_plan_nparams(plan.handle) == 1
+    L.tide_plan_destroy(None)
+
+
+def _ptrs(vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+# Fake, never-dereferenced device addresses: every call below must be
+# rejected by validation before the library touches the HIP runtime.
+A = 0x7F0000000000
+
+
+def _rs(plan, rank, grads, out, flags=0, max_wg=0):
+    return lib().tide_rs(plan.handle if plan else None, rank, grads,
+                         ctypes.c_void_p(out), flags, max_wg, None)
+
+
+def test_rs_argument_errors():
+    plan = tide.Plan([(4, 4), (8,)], 2)        # S = 8 + 4 = 12
+    good = _ptrs([A, A + 0x10000, A + 0x20000, A + 0x30000])
+    out = A + 0x100000
+    L = lib()
+    assert _rs(None, 0, good, out) == E_INVALID
+    assert _rs(plan, 2, good, out) == E_INVALID and b"rank" in L.tide_last_error()
+    assert _rs(plan, -1, good, out) == E_INVALID
+    assert _rs(plan, 0, good, out, flags=0x2) == E_UNSUPPORTED
+    assert _rs(plan, 0, good, out, max_wg=-1) == E_INVALID
+    assert _rs(plan, 0, None, out) == E_INVALID and b"grads" in L.tide_last_error()
+    assert _rs(plan, 0, good, 0) == E_INVALID and b"out is NULL" in L.tide_last_error()
+    assert _rs(plan, 0, good, out + 2) == E_INVALID and b"aligned" in L.tide_last_error()
+    assert _rs(plan, 0, _ptrs([A, None, A + 0x20000, A + 0x30000]), out) == E_INVALID
+    assert _rs(plan, 0, _ptrs([A + 1, A + 0x10000, A + 0x20000, A + 0x30000]), out) == E_INVALID
+    # out overlaps what rank 0 reads of rank 1's first gradient (elements 0..7)
+    assert _rs(plan, 0, good, A + 0x20000 + 8) == E_INVALID
+    assert b"overlaps" in L.tide_last_error()
+
+
+def test_rs_empty_plan_is_a_noop():
+    # S = 0: nothing to write, so nothing is launched and no HIP call is made.
+    plan = tide.Plan([(0, 3)], 4)
+    assert plan.S == 0
+    assert _rs(plan, 3, None, 0) == 0
+
+
+def _ag(plan, srcs, dsts, e=2, flags=0, max_wg=0):
+    return lib().tide_ag(plan.handle if plan else None, srcs, dsts, e, flags, max_wg, None)
+
+
+def test_ag_argument_errors():
+    plan = tide.Plan([(4, 4), (8,)], 2)        # S = 12; param sizes 16, 8
+    srcs = _ptrs([A, A + 0x1000])
+    dsts = _ptrs([A + 0x10000, A + 0x20000])
+    L = lib()
+    assert _ag(None, srcs, dsts) == E_INVALID
+    assert _ag(plan, srcs, dsts, e=3) == E_INVALID and b"elem_bytes" in L.tide_last_error()
+    assert _ag(plan, srcs, dsts, flags=0x8) == E_UNSUPPORTED
+    assert _ag(plan, srcs, dsts, max_wg=-5) == E_INVALID
+    assert _ag(plan, None, dsts) == E_INVALID
+    assert _ag(plan, srcs, None) == E_INVALID
+    assert _ag(plan, _ptrs([A, None]), dsts) == E_INVALID
+    assert _ag(plan, _ptrs([A + 1, A + 0x1000]), dsts) == E_INVALID
+    assert _ag(plan, srcs, _ptrs([A + 0x10000, A + 0x20002]), e=4) == E_INVALID
+    # destinations overlapping each other
+    assert _ag(plan, srcs, _ptrs([A + 0x10000, A + 0x10000 + 30])) == E_INVALID
+    assert b"overlaps" in L.tide_last_error()
+    # destination overlapping a source element that is read
+    assert _ag(plan, srcs, _ptrs([A + 0x10000, A + 0x1000 + 4])) == E_INVALID
+
+
+def test_ag_empty_plan_is_a_noop():
+    plan = tide.Plan([(0, 3), (0,)], 4)
+    assert _ag(plan, None, None) == 0
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    plan = tide.Plan([(4, 4)], 2)
+    cpu = [[torch.zeros(4, 4, dtype=torch.bfloat16)] for _ in range(2)]
+    with pytest.raises(ValueError):
+        tide.grad_table(plan, cpu)                   # not device tensors
+    with pytest.raises(TypeError):
+        tide.grad_table(plan, [[torch.zeros(4, 4)] for _ in range(2)])
+    with pytest.raises(ValueError):
+        tide.grad_table(plan, cpu[:1])

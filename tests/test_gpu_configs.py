@@ -1,0 +1,105 @@
+"""GPU parity at the full workload sizes, in the launch configurations the
+benchmark times (default grid and small-footprint grid).
+
+Workloads (architecture shapes only, synthetic seeded bf16 gradients):
+  * Llama-3-8B-shaped decoder layer, 8 ranks;
+  * Llama-3.1-70B-shaped decoder layer, 8 ranks;
+  * Qwen3-30B-A3B-shaped MoE layer (391 parameters, 6256 gradient
+    pointers), 16 ranks, 10% of experts all-zero per rank;
+  * Llama-3.1-70B-shaped layer at 64 ranks (~110 GB of gradients in HBM).
+
+The whole fp32 output block of each checked rank is compared bit for bit
+with the oracle, which reads host copies of exactly the gradient slices the
+rank reduces.  The all-gather placement is compared on every element of
+every parameter.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import parameter_layout_collectives_amd as tide
+import workloads
+from gpu_helpers import (BF16_SENTINEL, F32_SENTINEL, bits16, expected_rs, first_mismatch,
+                         note, same_f32)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+def _free():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _rs_cases(orc, w, grads, plan, table, ranks, modes):
+    out = torch.empty(plan.S, dtype=torch.float32, device=DEV)
+    for R in ranks:
+        want = expected_rs(orc, w.shapes, w.world, R, grads, plan)
+        for small in modes:
+            out.view(torch.int32).fill_(F32_SENTINEL)
+            note(f"{w.name}: tide_rs R={R} small={small}")
+            tide.rs(plan, R, table, out, small=small)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            assert same_f32(got, want), (w.name, R, small, first_mismatch(got, want))
+    return out
+
+
+def _ag_case(orc, w, plan):
+    N, S = w.world, plan.S
+    gathered = workloads.random_bf16(N * S, seed=4242, sigma=w.sigma, device=DEV)
+    params = [torch.full(s, 0, dtype=torch.int16, device=DEV).fill_(BF16_SENTINEL)
+              .view(torch.bfloat16) for s in w.shapes]
+    note(f"{w.name}: tide_ag N={N} S={S}")
+    tide.ag(plan, gathered, params)
+    torch.cuda.synchronize()
+    host = bits16(gathered)
+    want = orc.ag(w.shapes, N, [host[r * S:(r + 1) * S] for r in range(N)], elem_bytes=2)
+    for i, p in enumerate(params):
+        got = bits16(p).reshape(-1)
+        bad = np.nonzero(got != want[i])[0]
+        assert bad.size == 0, (w.name, i, int(bad[0]) if bad.size else None, bad.size)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama3_8b_layer", "llama31_70b_layer",
+                                  "qwen3_30b_a3b_moe_layer"])
+def test_workload_rs_ag(orc, name):
+    w = workloads.WORKLOADS[name]
+    note(f"{name}: generating {w.world} ranks of gradients on the device")
+    grads = workloads.all_grads(w, device=DEV)
+    plan = tide.Plan(w.shapes, w.world)
+    table = tide.grad_table(plan, grads)
+    out = _rs_cases(orc, w, grads, plan, table, sorted({0, 1, w.world - 1}), (False, True))
+    # determinism: the same call again gives the same bits
+    first = out.clone()
+    tide.rs(plan, w.world - 1, table, out)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int32), out.view(torch.int32))
+    del grads, table, out, first
+    _free()
+    _ag_case(orc, w, plan)
+    _free()
+
+
+@pytest.mark.timeout(900)
+def test_llama70b_layer_64_ranks(orc):
+    w = workloads.WORKLOADS["llama31_70b_layer_n64"]
+    note(f"{w.name}: generating {w.world} ranks of gradients on the device (~110 GB)")
+    grads = workloads.all_grads(w, device=DEV)
+    plan = tide.Plan(w.shapes, w.world)
+    table = tide.grad_table(plan, grads)
+    _rs_cases(orc, w, grads, plan, table, (0, 63), (False,))
+    _rs_cases(orc, w, grads, plan, table, (1,), (True,))
+    del grads, table
+    _free()

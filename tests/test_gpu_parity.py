@@ -1,0 +1,273 @@
+"""GPU parity of tide_rs / tide_ag against the CPU oracle at small sizes.
+
+Every case compares the HIP path with the oracle element by element on the
+same seeded inputs: bit-exact for the reduce-scatter (rank-order fp32 sum;
+NaN compared by class) and for the all-gather placement (a byte copy).
+Outputs are pre-filled with a sentinel so unwritten elements show up.
+
+Sizes span several tiles (4096 elements per reduce-scatter tile, 8192 per
+all-gather tile) with ragged tails, and cover the degenerate cases: empty
+parameters, 0-dim parameters, dim0 < N (ranks with no rows), N = 1, a single
+workgroup, unaligned pointers (scalar paths), alignment gaps, fp32 elements.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parameter_layout_collectives_amd as tide
+import workloads
+from gpu_helpers import (BF16_SENTINEL, F32_SENTINEL, bits16, bits32, expected_rs,
+                         first_mismatch, note, run_rs, same_f32)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+def to_dev(grads):
+    return [[g.to(DEV) for g in rank] for rank in grads]
+
+
+def fresh_out(S):
+    return torch.full((S,), F32_SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
+
+
+def check_rs(orc, shapes, N, grads_dev, R, align=1, **kw):
+    plan = tide.Plan(shapes, N, align)
+    out = fresh_out(plan.S)
+    note(f"tide_rs shapes={shapes} N={N} R={R} align={align} {kw}")
+    run_rs(plan, R, grads_dev, out, **kw)
+    want = expected_rs(orc, shapes, N, R, grads_dev, plan, align)
+    got = out.cpu().numpy()
+    assert same_f32(got, want), first_mismatch(got, want)
+    return got
+
+
+# ---------------------------------------------------------------------------
+# reduce-scatter
+# ---------------------------------------------------------------------------
+
+def test_tiny_every_rank(orc):
+    w = workloads.WORKLOADS["tiny"]
+    g = to_dev(workloads.all_grads(w))
+    for R in range(w.world):
+        for kw in ({}, {"small": True}, {"max_workgroups": 1}, {"max_workgroups": 3}):
+            check_rs(orc, w.shapes, w.world, g, R, **kw)
+
+
+RAGGED = [
+    [(4099, 3), (8191,), (1, 5), (12345, 2), (0, 4), (64, 64), ()],
+    [(33, 4), (2,), (70000,), (5, 1023)],
+]
+
+
+@pytest.mark.parametrize("case", range(len(RAGGED)))
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 13, 16])
+def test_ragged_shapes(orc, case, N):
+    shapes = RAGGED[case]
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=100 * N + case))
+    for R in sorted({0, 1 % N, N // 2, N - 1}):
+        check_rs(orc, shapes, N, g, R)
+
+
+@pytest.mark.parametrize("align", [4, 6, 64])
+def test_alignment_gaps(orc, align):
+    shapes = [(37, 3), (16,), (9, 9), (3,)]
+    N = 4
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=7))
+    for R in range(N):
+        check_rs(orc, shapes, N, g, R, align=align)
+
+
+def test_many_ranks_and_tiny_params(orc):
+    shapes = [(1,), (3,), (200, 7), (64,)]
+    N = 64
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=3))
+    for R in (0, 1, 2, 63):
+        check_rs(orc, shapes, N, g, R)
+        check_rs(orc, shapes, N, g, R, small=True)
+
+
+def test_unaligned_pointers(orc):
+    """Gradients at odd element offsets inside bigger buffers (2-byte
+    aligned, not 16), with every rank at a different offset, and an output
+    that is 4-byte but not 16-byte aligned: all scalar paths."""
+    shapes = [(513, 5), (4100,), (7, 3)]
+    N = 5
+    host = workloads.random_grads_for_shapes(shapes, N, seed_base=55)
+    grads = []
+    for r, rank in enumerate(host):
+        row = []
+        for i, t in enumerate(rank):
+            n = t.numel()
+            buf = torch.zeros(n + 16, dtype=torch.bfloat16, device=DEV)
+            shift = (r + 3 * i) % 8 + 1
+            view = buf[shift:shift + n]
+            view.copy_(t.reshape(-1).to(DEV))
+            row.append(view.view(t.shape))
+        grads.append(row)
+    plan = tide.Plan(shapes, N)
+    for R in range(N):
+        big = fresh_out(plan.S + 3)
+        out = big[1:1 + plan.S]
+        note(f"tide_rs unaligned R={R}")
+        run_rs(plan, R, grads, out)
+        want = expected_rs(orc, shapes, N, R, grads, plan)
+        got = out.cpu().numpy()
+        assert same_f32(got, want), first_mismatch(got, want)
+        assert bits32(big[0:1])[0] == F32_SENTINEL
+        assert bits32(big[-2:])[1] == F32_SENTINEL
+
+
+def test_aligned_inputs_unaligned_output(orc):
+    shapes = [(1000, 8), (4096,)]
+    N = 4
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=9))
+    plan = tide.Plan(shapes, N)
+    big = fresh_out(plan.S + 2)
+    out = big[1:1 + plan.S]
+    for R in range(N):
+        run_rs(plan, R, g, out)
+        want = expected_rs(orc, shapes, N, R, g, plan)
+        got = out.cpu().numpy()
+        assert same_f32(got, want), first_mismatch(got, want)
+
+
+def test_special_values(orc):
+    """-0.0, bf16 subnormals, +-Inf and NaN go through the vector path."""
+    N = 4
+    n = 4096 + 24
+    pool = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x7F80, 0xFF80,
+                     0x7FC0, 0x3F80, 0xBF80, 0x4B80, 0xCB80, 0x7F7F, 0xFF7F], np.uint16)
+    rng = np.random.default_rng(1)
+    grads = []
+    for r in range(N):
+        bits = pool[rng.integers(0, len(pool), size=n)]
+        bits[:64] = 0x8000                      # columns of -0.0 only
+        bits[64:128] = 0x0001                   # subnormal sums, exact
+        t = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(DEV)
+        grads.append([t.reshape(n // 4, 4)])
+    for R in range(N):
+        got = check_rs(orc, [(n // 4, 4)], N, grads, R)
+        if R == 0:
+            assert np.all(got[:64].view(np.uint32) == 0x80000000)
+            assert np.all(got[64:128].view(np.uint32) == (N << 16))
+
+
+def test_integer_values_exact(orc):
+    N = 16
+    shapes = [(300, 17), (4096,)]
+    rng = np.random.default_rng(3)
+    ints = [[rng.integers(-8, 9, size=s) for s in shapes] for _ in range(N)]
+    grads = [[torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(DEV) for a in rank]
+             for rank in ints]
+    plan = tide.Plan(shapes, N)
+    for R in (0, 7, 15):
+        out = fresh_out(plan.S)
+        run_rs(plan, R, grads, out)
+        got = out.cpu().numpy()
+        for i, s in enumerate(shapes):
+            src, L = plan.real(R, i)
+            off = plan.param(i)[0]
+            want = sum(ints[r][i].reshape(-1)[src:src + L].astype(np.int64) for r in range(N))
+            assert np.array_equal(got[off:off + L].astype(np.int64), want)
+
+
+def test_deterministic_and_streams(orc):
+    shapes = [(4096, 33), (77,)]
+    N = 8
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=21))
+    plan = tide.Plan(shapes, N)
+    table = tide.grad_table(plan, g)
+    a = fresh_out(plan.S)
+    b = fresh_out(plan.S)
+    s = torch.cuda.Stream()
+    tide.rs(plan, 3, table, a)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        tide.rs(plan, 3, table, b, stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    want = expected_rs(orc, shapes, N, 3, g, plan)
+    assert same_f32(a.cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------------------
+# all-gather placement
+# ---------------------------------------------------------------------------
+
+def check_ag(orc, shapes, N, e=2, align=1, src_shift=0, dst_shift=0, **kw):
+    plan = tide.Plan(shapes, N, align)
+    S = plan.S
+    dt = torch.bfloat16 if e == 2 else torch.float32
+    ft = torch.int16 if e == 2 else torch.int32
+    sentinel = BF16_SENTINEL if e == 2 else F32_SENTINEL
+    rng = np.random.default_rng(N * 7 + e + align)
+    flat_bits = rng.integers(0, 2 ** (8 * e) - 1, size=N * S + src_shift, dtype=np.uint64)
+    flat_bits = flat_bits.astype(np.uint16 if e == 2 else np.uint32)
+    buf = torch.from_numpy(flat_bits.view(np.int16 if e == 2 else np.int32)).to(DEV).view(dt)
+    gathered = buf[src_shift:src_shift + N * S]
+    blocks = [gathered[r * S:(r + 1) * S] for r in range(N)]
+    params, bases = [], []
+    for s in shapes:
+        n = int(np.prod(s)) if len(s) else 1
+        base = torch.full((n + dst_shift + 1,), sentinel, dtype=ft, device=DEV).view(dt)
+        bases.append(base)
+        params.append(base[dst_shift:dst_shift + n].view(s if len(s) else ()))
+    note(f"tide_ag shapes={shapes} N={N} e={e} align={align} shifts={src_shift},{dst_shift} {kw}")
+    tide.ag(plan, blocks, params, **kw)
+    torch.cuda.synchronize()
+    host_blocks = [flat_bits[src_shift + r * S: src_shift + (r + 1) * S] for r in range(N)]
+    want = orc.ag(shapes, N, host_blocks, elem_bytes=e, align=align)
+    for i, p in enumerate(params):
+        got = (bits16(p) if e == 2 else bits32(p)).reshape(-1)
+        bad = np.nonzero(got != want[i])[0]
+        assert bad.size == 0, (i, int(bad[0]), bad.size)
+        tail = (bits16(bases[i]) if e == 2 else bits32(bases[i]))
+        assert np.all(tail[:dst_shift] == sentinel) and tail[-1] == sentinel
+
+
+def test_ag_tiny(orc):
+    w = workloads.WORKLOADS["tiny"]
+    for kw in ({}, {"small": True}, {"max_workgroups": 1}):
+        check_ag(orc, w.shapes, w.world, **kw)
+
+
+@pytest.mark.parametrize("N", [1, 3, 8, 16])
+@pytest.mark.parametrize("e", [2, 4])
+def test_ag_ragged(orc, N, e):
+    check_ag(orc, RAGGED[0], N, e=e)
+    check_ag(orc, RAGGED[1], N, e=e, align=8)
+
+
+@pytest.mark.parametrize("src_shift,dst_shift", [(1, 0), (0, 3), (5, 5), (2, 6), (4, 0)])
+@pytest.mark.parametrize("e", [2, 4])
+def test_ag_unaligned(orc, src_shift, dst_shift, e):
+    check_ag(orc, [(1031, 3), (9000,), (5, 5)], 4, e=e, src_shift=src_shift,
+             dst_shift=dst_shift)
+
+
+def test_ag_inverts_rs_layout(orc):
+    """AG of the fp32 blocks tide_rs wrote for every rank equals the
+    rank-order all-reduce of the gradients (reduce-scatter + all-gather)."""
+    shapes = [(5, 7), (16,), (33, 4), (4097,)]
+    N = 4
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=31))
+    plan = tide.Plan(shapes, N)
+    blocks = torch.empty(N, plan.S, dtype=torch.float32, device=DEV)
+    for R in range(N):
+        tide.rs(plan, R, g, blocks[R])
+    params = [torch.empty(s, dtype=torch.float32, device=DEV) for s in shapes]
+    tide.ag(plan, blocks, params)
+    torch.cuda.synchronize()
+    host = [[bits16(t) for t in rank] for rank in g]
+    want_blocks = [orc.rs(shapes, N, R, host).view(np.uint32) for R in range(N)]
+    want = orc.ag(shapes, N, want_blocks, elem_bytes=4)
+    for i in range(len(shapes)):
+        assert np.array_equal(bits32(params[i]).reshape(-1), want[i]), i
