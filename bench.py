@@ -178,7 +178,7 @@ def counter_traffic(kernel):
 # co-run with a bf16 GEMM
 # ---------------------------------------------------------------------------
 
-def corun(w, gemm_shape, gemm_reps=20, modes=(False, True)):
+def corun(w, gemm_shape, gemm_reps=30, modes=(False, True), repeats=2):
     M, K, Nn = gemm_shape
     N = w.world
     log(f"co-run: generating {w.name} ({N} ranks) and a bf16 {M}x{K}x{Nn} GEMM")
@@ -223,50 +223,63 @@ def corun(w, gemm_shape, gemm_reps=20, modes=(False, True)):
     t_gemm = statistics.median(alone)
     res = {"gemm": f"bf16 {M}x{K}x{Nn} torch.matmul", "gemm_alone_ms": t_gemm,
            "gemm_tflops_alone": 2.0 * M * K * Nn / (t_gemm * 1e-3) / 1e12,
-           "workload": w.name, "world": N}
+           "workload": w.name, "world": N, "repeats": repeats,
+           "method": ("stream A runs the GEMMs, stream B a chain of tide_rs calls (rank "
+                      "rotating) started first and long enough to cover them; slowdown = "
+                      "median GEMM time while tide_rs runs / median GEMM time alone - 1, "
+                      "counting only GEMMs that start and end inside the tide_rs window")}
     for small in modes:
         t_rs = rs_alone(small)
-        n_rs = int(1.5 * (gemm_reps + 4) * t_gemm / t_rs) + 4
-        base = torch.cuda.Event(enable_timing=True)
-        rs_start = torch.cuda.Event(enable_timing=True)
-        rs_end = torch.cuda.Event(enable_timing=True)
-        first_done = torch.cuda.Event()
-        ev = timed_events(gemm_reps)
-        torch.cuda.synchronize()
-        base.record()
-        sb.wait_stream(torch.cuda.current_stream())
-        sa.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(sb):
-            rs_start.record()
-            tide.rs(plan, 0, table, out[0], small=small, stream=sb)
-            first_done.record()
-            for k in range(1, n_rs):
-                tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
-            rs_end.record()
-        with torch.cuda.stream(sa):
-            sa.wait_event(first_done)
-            for _ in range(2):
-                torch.matmul(A, B, out=C)
-            for s, e in ev:
-                s.record()
-                torch.matmul(A, B, out=C)
-                e.record()
-        torch.cuda.synchronize()
-        rs_lo = base.elapsed_time(rs_start)
-        rs_hi = base.elapsed_time(rs_end)
-        inside = [s.elapsed_time(e) for s, e in ev
-                  if base.elapsed_time(s) >= rs_lo and base.elapsed_time(e) <= rs_hi]
         key = "small_footprint" if small else "default"
-        med = statistics.median(inside) if inside else None
+        runs = []
+        for _ in range(repeats):
+            n_rs = int(1.5 * (gemm_reps + 4) * t_gemm / t_rs) + 4
+            base = torch.cuda.Event(enable_timing=True)
+            rs_start = torch.cuda.Event(enable_timing=True)
+            rs_end = torch.cuda.Event(enable_timing=True)
+            first_done = torch.cuda.Event()
+            ev = timed_events(gemm_reps)
+            torch.cuda.synchronize()
+            base.record()
+            sb.wait_stream(torch.cuda.current_stream())
+            sa.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(sb):
+                rs_start.record()
+                tide.rs(plan, 0, table, out[0], small=small, stream=sb)
+                first_done.record()
+                for k in range(1, n_rs):
+                    tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
+                rs_end.record()
+            with torch.cuda.stream(sa):
+                sa.wait_event(first_done)
+                for _ in range(2):
+                    torch.matmul(A, B, out=C)
+                for s, e in ev:
+                    s.record()
+                    torch.matmul(A, B, out=C)
+                    e.record()
+            torch.cuda.synchronize()
+            rs_lo = base.elapsed_time(rs_start)
+            rs_hi = base.elapsed_time(rs_end)
+            inside = [s.elapsed_time(e) for s, e in ev
+                      if base.elapsed_time(s) >= rs_lo and base.elapsed_time(e) <= rs_hi]
+            med = statistics.median(inside) if inside else None
+            runs.append({
+                "gemm_corun_ms": med,
+                "gemms_fully_overlapped": len(inside),
+                "gemm_slowdown_pct": None if med is None else 100.0 * (med / t_gemm - 1.0),
+                "tide_rs_corun_GBps": n_rs * b_rs / ((rs_hi - rs_lo) * 1e-3) / 1e9,
+            })
+        slow = [r["gemm_slowdown_pct"] for r in runs if r["gemm_slowdown_pct"] is not None]
         res[key] = {
             "tide_rs_alone_us": t_rs * 1e3,
             "tide_rs_alone_GBps": b_rs / (t_rs * 1e-3) / 1e9,
-            "tide_rs_corun_GBps": n_rs * b_rs / ((rs_hi - rs_lo) * 1e-3) / 1e9,
-            "gemm_corun_ms": med,
-            "gemms_fully_overlapped": len(inside),
-            "gemm_slowdown_pct": None if med is None else 100.0 * (med / t_gemm - 1.0),
+            "tide_rs_corun_GBps": statistics.median(r["tide_rs_corun_GBps"] for r in runs),
+            "gemm_slowdown_pct": statistics.median(slow) if slow else None,
+            "runs": runs,
         }
-        log(f"co-run {key}: {res[key]}")
+        log(f"co-run {key}: slowdown {res[key]['gemm_slowdown_pct']:.2f}% "
+            f"(runs {[round(x, 2) for x in slow]}), tide_rs {res[key]['tide_rs_corun_GBps']:.0f} GB/s")
     del grads, table, out, A, B, C
     return res
 

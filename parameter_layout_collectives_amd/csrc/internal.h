@@ -14,11 +14,21 @@
 
 namespace tide {
 
+// Build-time tuning constants (defaults are the measured best on MI355X).
+#ifndef TIDE_RS_TILE
+#define TIDE_RS_TILE 4096
+#endif
+#ifndef TIDE_AG_TILE
+#define TIDE_AG_TILE 2048
+#endif
+
 // Elements of one parameter segment handled by one reduce-scatter tile, and
 // by one all-gather tile.  Both are multiples of 8 so that tile starts keep
 // the 16-byte phase of the segment they cut.
-constexpr int64_t kRsTile = 4096;
-constexpr int64_t kAgTile = 8192;
+constexpr int64_t kRsTile = TIDE_RS_TILE;
+constexpr int64_t kAgTile = TIDE_AG_TILE;
+static_assert(kRsTile % 8 == 0 && kAgTile % 8 == 0, "tiles must keep the 16-byte phase");
+static_assert(kAgTile * 4 < (int64_t(1) << 31), "all-gather tile bytes must fit in int");
 constexpr int kBlock = 256;           // lanes per workgroup (4 wave64)
 
 // Per-parameter geometry as the kernels read it.  src(r) = r*seg and
@@ -50,6 +60,9 @@ struct PtrTable {
 struct DeviceState {
     int device = -1;
     int cus = 0;
+    int lds_per_cu = 0;          // bytes of LDS per compute unit
+    int lds_per_wg_max = 0;      // largest LDS allocation one workgroup may make
+    int small_lds = 0;           // LDS a small-footprint workgroup reserves (0 = none)
     void *d_params = nullptr;    // ParamDesc[P]
     void *d_rs_tiles = nullptr;  // Tile[n_rs]
     void *d_ag_tiles = nullptr;  // Tile[n_ag]

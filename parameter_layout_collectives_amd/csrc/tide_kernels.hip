@@ -47,6 +47,32 @@ __device__ __forceinline__ GLOBAL_AS T *gstore_ptr(void *p) {
 // Device helpers
 // ---------------------------------------------------------------------------
 
+#ifndef TIDE_NT_LOAD
+#define TIDE_NT_LOAD 1
+#endif
+#ifndef TIDE_NT_STORE
+#define TIDE_NT_STORE 1
+#endif
+
+// Streaming loads and stores: data touched once carries the non-temporal
+// hint so it does not push a concurrent kernel's working set out of cache.
+template <class V>
+__device__ __forceinline__ V stream_load(const GLOBAL_AS V *p) {
+#if TIDE_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+template <class V>
+__device__ __forceinline__ void stream_store(V v, GLOBAL_AS V *p) {
+#if TIDE_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
 // bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -54,57 +80,79 @@ __device__ __forceinline__ float bf16_at(const uint16_t *p) {
     return __uint_as_float(static_cast<uint32_t>(*gload_ptr<uint16_t>(p)) << 16);
 }
 
+// Four fp32 values from two words holding four consecutive bf16 (the element
+// with the lower address sits in the low half of its word).
+__device__ __forceinline__ f32x4 widen4(uint32_t w0, uint32_t w1) {
+    return f32x4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+}
+
 // Scalar path for elements [a, b) of a segment: one lane per element, the
 // same rank-order sum as the vector path.
+template <int BLOCK>
 __device__ __forceinline__ void rs_elems(const uint16_t *const *__restrict__ P, int N,
                                          int64_t src, float *__restrict__ o, int64_t a,
                                          int64_t b) {
-    for (int64_t k = a + threadIdx.x; k < b; k += kBlock) {
+    for (int64_t k = a + threadIdx.x; k < b; k += BLOCK) {
         float acc = bf16_at(P[0] + src + k);
         for (int r = 1; r < N; r++) acc = acc + bf16_at(P[r] + src + k);
         o[k] = acc;
     }
 }
 
-// Loads one batch of up to 8 ranks (16 bytes = 8 bf16 per lane and chunk),
-// all issued before any add, then adds them in rank order.  FIRST: the batch
-// starts at rank 0, whose value initialises the sums.
-// `first` = src + (first element of this tile's vector range): a
-// wave-uniform element offset; lane_off[j] is each lane's chunk start
-// relative to it, in bytes (< 32 bits).
-template <int CPL, bool FIRST>
+// VEC consecutive bf16 per lane and chunk: 16-byte loads for VEC = 8,
+// 8-byte loads for VEC = 4.
+template <int VEC> struct RsIn;
+template <> struct RsIn<8> { typedef u32x4 type; };
+template <> struct RsIn<4> { typedef u32x2 type; };
+
+// Loads one batch of up to RB ranks, all issued before any add, then adds
+// them in rank order.  FIRST: the batch starts at rank 0, whose value
+// initialises the sums.  `first` = src + (first element of this tile's
+// vector range), wave-uniform; lane_off[j] is each lane's chunk start
+// relative to it, in bytes (fits in 32 bits).
+template <int CPL, int VEC, int RB, bool FIRST>
 __device__ __forceinline__ void rs_batch(const uint16_t *const *__restrict__ P, int r0, int nb,
-                                         int64_t first, const uint32_t *lane_off, f32x4 *a0,
-                                         f32x4 *a1) {
-    u32x4 v[8][CPL];
+                                         int64_t first, const uint32_t *lane_off,
+                                         f32x4 (*acc)[VEC / 4]) {
+    typedef typename RsIn<VEC>::type V;
+    V v[RB][CPL];
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
+    for (int q = 0; q < RB; q++) {
         if (q < nb) {
             const GLOBAL_AS char *base = gload_ptr<char>(P[r0 + q] + first);
 #pragma unroll
             for (int j = 0; j < CPL; j++)
-                v[q][j] = __builtin_nontemporal_load(
-                    reinterpret_cast<const GLOBAL_AS u32x4 *>(base + lane_off[j]));
+                v[q][j] = stream_load(reinterpret_cast<const GLOBAL_AS V *>(base + lane_off[j]));
         }
     }
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
+    for (int q = 0; q < RB; q++) {
         if (q < nb) {
 #pragma unroll
             for (int j = 0; j < CPL; j++) {
-                const u32x4 w = v[q][j];
-                const f32x4 x0 = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-                const f32x4 x1 = {bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-                if (FIRST && q == 0) {
-                    a0[j] = x0;
-                    a1[j] = x1;
-                } else {
-                    a0[j] = a0[j] + x0;
-                    a1[j] = a1[j] + x1;
+#pragma unroll
+                for (int h = 0; h < VEC / 4; h++) {
+                    const f32x4 x = widen4(v[q][j][2 * h], v[q][j][2 * h + 1]);
+                    if (FIRST && q == 0)
+                        acc[j][h] = x;
+                    else
+                        acc[j][h] = acc[j][h] + x;
                 }
             }
         }
     }
+}
+
+// Workgroup IDs are dealt to the 8 XCDs round-robin (ID mod 8), and each XCD
+// has its own L2.  Virtual index v is mapped so that the workgroups of one
+// XCD take one contiguous eighth of the tile list: tile-table lines and the
+// data of neighbouring tiles are then fetched into one L2, not all eight.
+// The map is a bijection on [0, ntiles) for any tile count.
+constexpr int64_t kXcds = 8;
+__device__ __forceinline__ int64_t xcd_tile(int64_t v, int64_t ntiles) {
+    const int64_t q = ntiles / kXcds, rm = ntiles % kXcds;
+    const int64_t x = v % kXcds, j = v / kXcds;
+    return x * q + (x < rm ? x : rm) + j;
 }
 
 // ---------------------------------------------------------------------------
@@ -118,19 +166,21 @@ __device__ __forceinline__ void rs_batch(const uint16_t *const *__restrict__ P, 
 // ptrs is param-major: ptrs[i*N + r] = G[r][i].
 //
 // vec_in: every gradient pointer is 16-byte aligned, so lanes take chunks of
-// 8 elements whose source address is 16-byte aligned (k + src = 0 mod 8);
-// the few elements before the first and after the last chunk of a tile take
-// the scalar path.  vec_out: `out` is 16-byte aligned; a chunk is stored as
-// two 16-byte stores when its output offset is a multiple of 4 too.
-template <int CPL>
-__global__ __launch_bounds__(kBlock) void rs_kernel(const ParamDesc *__restrict__ pdesc,
-                                                    const Tile *__restrict__ tiles,
-                                                    int64_t ntiles,
-                                                    const uint16_t *const *__restrict__ ptrs,
-                                                    int N, int R, float *__restrict__ out,
-                                                    int vec_in, int vec_out) {
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const Tile tile = tiles[t];
+// VEC elements whose source address is VEC*2-byte aligned; the few elements
+// before the first and after the last chunk of a tile take the scalar path.
+// vec_out: `out` is 16-byte aligned; a chunk's VEC fp32 results go out as
+// 16-byte stores when its output offset is a multiple of 4 too.  With VEC = 4
+// every store instruction of a wave covers one contiguous 1 KiB span.
+// PACE > 0 makes each wave sleep between tiles (small-footprint launches).
+template <int BLOCK, int CPL, int VEC, int RB, int PACE, bool XMAP>
+__global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__ pdesc,
+                                                   const Tile *__restrict__ tiles,
+                                                   int64_t ntiles,
+                                                   const uint16_t *const *__restrict__ ptrs,
+                                                   int N, int R, float *__restrict__ out,
+                                                   int vec_in, int vec_out) {
+    for (int64_t v = blockIdx.x; v < ntiles; v += gridDim.x) {
+        const Tile tile = tiles[XMAP ? xcd_tile(v, ntiles) : v];
         const ParamDesc d = pdesc[tile.param];
         const int64_t src = static_cast<int64_t>(R) * d.seg;
         int64_t L = d.numel - src;
@@ -144,54 +194,57 @@ __global__ __launch_bounds__(kBlock) void rs_kernel(const ParamDesc *__restrict_
         if (kb < re) {
             int64_t vs = re, ve = re;
             if (vec_in) {
-                vs = min(re, kb + ((8 - ((src + kb) & 7)) & 7));
-                ve = vs + ((re - vs) & ~static_cast<int64_t>(7));
+                vs = min(re, kb + ((VEC - ((src + kb) & (VEC - 1))) & (VEC - 1)));
+                ve = vs + ((re - vs) & ~static_cast<int64_t>(VEC - 1));
             }
-            rs_elems(P, N, src, o, kb, vs);
-            rs_elems(P, N, src, o, ve, re);
+            rs_elems<BLOCK>(P, N, src, o, kb, vs);
+            rs_elems<BLOCK>(P, N, src, o, ve, re);
 
-            // A tile holds at most kRsTile/8 chunks, so every per-lane byte
-            // offset below fits in 32 bits.
-            const int nch = static_cast<int>((ve - vs) >> 3);
+            // A tile holds at most kRsTile/VEC chunks, so every per-lane
+            // byte offset below fits in 32 bits.
+            const int nch = static_cast<int>((ve - vs) / VEC);
             const bool st16 = vec_out && (((d.off + vs) & 3) == 0);
             GLOBAL_AS char *obase = gstore_ptr<char>(o + vs);
-            for (int c0 = 0; c0 < nch; c0 += kBlock * CPL) {
+            for (int c0 = 0; c0 < nch; c0 += BLOCK * CPL) {
                 uint32_t in_off[CPL], out_off[CPL];
                 bool ok[CPL];
 #pragma unroll
                 for (int j = 0; j < CPL; j++) {
-                    const int ch = c0 + j * kBlock + static_cast<int>(threadIdx.x);
+                    const int ch = c0 + j * BLOCK + static_cast<int>(threadIdx.x);
                     ok[j] = ch < nch;
                     // Lanes past the end re-read the last chunk (in bounds)
                     // and do not store.
                     const uint32_t c = static_cast<uint32_t>(ok[j] ? ch : nch - 1);
-                    in_off[j] = c * 16u;     // 8 bf16
-                    out_off[j] = c * 32u;    // 8 fp32
+                    in_off[j] = c * (2u * VEC);
+                    out_off[j] = c * (4u * VEC);
                 }
-                f32x4 a0[CPL], a1[CPL];
-                rs_batch<CPL, true>(P, 0, min(N, 8), src + vs, in_off, a0, a1);
-                for (int r0 = 8; r0 < N; r0 += 8)
-                    rs_batch<CPL, false>(P, r0, min(N - r0, 8), src + vs, in_off, a0, a1);
+                f32x4 acc[CPL][VEC / 4];
+                rs_batch<CPL, VEC, RB, true>(P, 0, min(N, RB), src + vs, in_off, acc);
+                for (int r0 = RB; r0 < N; r0 += RB)
+                    rs_batch<CPL, VEC, RB, false>(P, r0, min(N - r0, RB), src + vs, in_off, acc);
 #pragma unroll
                 for (int j = 0; j < CPL; j++) {
                     if (!ok[j]) continue;
                     if (st16) {
                         GLOBAL_AS f32x4 *dst =
                             reinterpret_cast<GLOBAL_AS f32x4 *>(obase + out_off[j]);
-                        __builtin_nontemporal_store(a0[j], dst);
-                        __builtin_nontemporal_store(a1[j], dst + 1);
+#pragma unroll
+                        for (int h = 0; h < VEC / 4; h++) stream_store(acc[j][h], dst + h);
                     } else {
                         GLOBAL_AS float *dst = reinterpret_cast<GLOBAL_AS float *>(obase + out_off[j]);
 #pragma unroll
-                        for (int e = 0; e < 4; e++) {
-                            dst[e] = a0[j][e];
-                            dst[4 + e] = a1[j][e];
-                        }
+                        for (int h = 0; h < VEC / 4; h++)
+#pragma unroll
+                            for (int e = 0; e < 4; e++) dst[4 * h + e] = acc[j][h][e];
                     }
                 }
             }
         }
-        for (int64_t k = max(kb, L) + threadIdx.x; k < ke; k += kBlock) o[k] = 0.0f;
+        for (int64_t k = max(kb, L) + threadIdx.x; k < ke; k += BLOCK) o[k] = 0.0f;
+        if (PACE > 0) {
+#pragma unroll
+            for (int p = 0; p < PACE; p++) __builtin_amdgcn_s_sleep(32);
+        }
     }
 }
 
@@ -206,15 +259,16 @@ template <> struct VecOf<4> { typedef uint32_t type; };
 template <> struct VecOf<2> { typedef uint16_t type; };
 
 // Copies bytes [a, b) of a span element by element (e = 2 or 4 bytes).
+template <int BLOCK>
 __device__ __forceinline__ void copy_elems(const char *s, char *d, int a, int b, int e) {
     const GLOBAL_AS char *gs = gload_ptr<char>(s);
     GLOBAL_AS char *gd = gstore_ptr<char>(d);
     if (e == 2) {
-        for (int x = a + 2 * static_cast<int>(threadIdx.x); x < b; x += 2 * kBlock)
+        for (int x = a + 2 * static_cast<int>(threadIdx.x); x < b; x += 2 * BLOCK)
             *reinterpret_cast<GLOBAL_AS uint16_t *>(gd + x) =
                 *reinterpret_cast<const GLOBAL_AS uint16_t *>(gs + x);
     } else {
-        for (int x = a + 4 * static_cast<int>(threadIdx.x); x < b; x += 4 * kBlock)
+        for (int x = a + 4 * static_cast<int>(threadIdx.x); x < b; x += 4 * BLOCK)
             *reinterpret_cast<GLOBAL_AS uint32_t *>(gd + x) =
                 *reinterpret_cast<const GLOBAL_AS uint32_t *>(gs + x);
     }
@@ -224,42 +278,42 @@ __device__ __forceinline__ void copy_elems(const char *s, char *d, int a, int b,
 // first W-aligned destination byte, W-byte vectors (U per lane in flight),
 // element-wise tail.
 // n is at most kAgTile * 4 bytes, so lane offsets fit in 32 bits.
-template <int W, int U>
+template <int BLOCK, int W, int U>
 __device__ __forceinline__ void copy_span_w(const char *s, char *d, int n, int e) {
     typedef typename VecOf<W>::type V;
     const int h = min(n, static_cast<int>((W - (reinterpret_cast<uintptr_t>(d) & (W - 1))) &
                                           (W - 1)));
-    copy_elems(s, d, 0, h, e);
+    copy_elems<BLOCK>(s, d, 0, h, e);
     const int nv = (n - h) / W;
     const GLOBAL_AS V *vs = gload_ptr<V>(s + h);
     GLOBAL_AS V *vd = gstore_ptr<V>(d + h);
-    for (int b = 0; b < nv; b += kBlock * U) {
+    for (int b = 0; b < nv; b += BLOCK * U) {
         V v[U];
 #pragma unroll
         for (int j = 0; j < U; j++) {
-            const int i = b + j * kBlock + static_cast<int>(threadIdx.x);
-            if (i < nv) v[j] = __builtin_nontemporal_load(vs + i);
+            const int i = b + j * BLOCK + static_cast<int>(threadIdx.x);
+            if (i < nv) v[j] = stream_load(vs + i);
         }
 #pragma unroll
         for (int j = 0; j < U; j++) {
-            const int i = b + j * kBlock + static_cast<int>(threadIdx.x);
-            if (i < nv) __builtin_nontemporal_store(v[j], vd + i);
+            const int i = b + j * BLOCK + static_cast<int>(threadIdx.x);
+            if (i < nv) stream_store(v[j], vd + i);
         }
     }
-    copy_elems(s, d, h + nv * W, n, e);
+    copy_elems<BLOCK>(s, d, h + nv * W, n, e);
 }
 
 // Tile t covers elements [k0, k0 + kAgTile) of rank r's shard of parameter
 // i: they move from rank_src[r] + off_i + k to params[i] + r*seg_i + k.
 // ptrs = rank_src[0..N) followed by params[0..P).
-template <int U>
-__global__ __launch_bounds__(kBlock) void ag_kernel(const ParamDesc *__restrict__ pdesc,
+template <int BLOCK, int U, int PACE, bool XMAP>
+__global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__ pdesc,
                                                     const Tile *__restrict__ tiles,
                                                     int64_t ntiles,
                                                     const uintptr_t *__restrict__ ptrs, int N,
                                                     int e) {
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const Tile tile = tiles[t];
+    for (int64_t v = blockIdx.x; v < ntiles; v += gridDim.x) {
+        const Tile tile = tiles[XMAP ? xcd_tile(v, ntiles) : v];
         const ParamDesc d = pdesc[tile.param];
         const int64_t src = static_cast<int64_t>(tile.rank) * d.seg;
         int64_t L = d.numel - src;
@@ -270,13 +324,17 @@ __global__ __launch_bounds__(kBlock) void ag_kernel(const ParamDesc *__restrict_
         const int n = static_cast<int>(len * e);
         const uintptr_t diff = reinterpret_cast<uintptr_t>(s) ^ reinterpret_cast<uintptr_t>(dst);
         if ((diff & 15) == 0)
-            copy_span_w<16, U>(s, dst, n, e);
+            copy_span_w<BLOCK, 16, U>(s, dst, n, e);
         else if ((diff & 7) == 0)
-            copy_span_w<8, U>(s, dst, n, e);
+            copy_span_w<BLOCK, 8, U>(s, dst, n, e);
         else if ((diff & 3) == 0)
-            copy_span_w<4, U>(s, dst, n, e);
+            copy_span_w<BLOCK, 4, U>(s, dst, n, e);
         else
-            copy_span_w<2, U>(s, dst, n, e);
+            copy_span_w<BLOCK, 2, U>(s, dst, n, e);
+        if (PACE > 0) {
+#pragma unroll
+            for (int p = 0; p < PACE; p++) __builtin_amdgcn_s_sleep(32);
+        }
     }
 }
 
@@ -284,10 +342,61 @@ __global__ __launch_bounds__(kBlock) void ag_kernel(const ParamDesc *__restrict_
 // Host side: per-device tables, pointer-table cache, launch policy
 // ---------------------------------------------------------------------------
 
-constexpr int kRsChunksPerLane = 2;
-constexpr int kAgVecsPerLane = 4;
-constexpr int kWgPerCu = 8;           // default grid: enough waves to keep HBM busy
-constexpr int kSmallFootprintWg = 32; // small-footprint grid (4 per XCD)
+#ifndef TIDE_RS_CPL
+#define TIDE_RS_CPL 4
+#endif
+#ifndef TIDE_RS_VEC
+#define TIDE_RS_VEC 4
+#endif
+#ifndef TIDE_DEFAULT_ONE_TILE_PER_WG
+#define TIDE_DEFAULT_ONE_TILE_PER_WG 1
+#endif
+#ifndef TIDE_SMALL_BLOCK
+#define TIDE_SMALL_BLOCK 256
+#endif
+#ifndef TIDE_SMALL_PACE
+#define TIDE_SMALL_PACE 0
+#endif
+#ifndef TIDE_SMALL_LDS_RESERVE
+#define TIDE_SMALL_LDS_RESERVE 1
+#endif
+#ifndef TIDE_SMALL_WG_PER_CU
+#define TIDE_SMALL_WG_PER_CU 1
+#endif
+#ifndef TIDE_RS_RB
+#define TIDE_RS_RB 8
+#endif
+#ifndef TIDE_SMALL_CPL
+#define TIDE_SMALL_CPL 4
+#endif
+#ifndef TIDE_SMALL_VEC
+#define TIDE_SMALL_VEC 4
+#endif
+#ifndef TIDE_SMALL_RB
+#define TIDE_SMALL_RB 8
+#endif
+#ifndef TIDE_SMALL_PERSISTENT
+#define TIDE_SMALL_PERSISTENT 0
+#endif
+#ifndef TIDE_XMAP_RS
+#define TIDE_XMAP_RS 0
+#endif
+#ifndef TIDE_XMAP_AG
+#define TIDE_XMAP_AG 1
+#endif
+#ifndef TIDE_AG_U
+#define TIDE_AG_U 1
+#endif
+#ifndef TIDE_WG_PER_CU
+#define TIDE_WG_PER_CU 8
+#endif
+#ifndef TIDE_SMALL_WG
+#define TIDE_SMALL_WG 32
+#endif
+constexpr int kRsChunksPerLane = TIDE_RS_CPL;
+constexpr int kAgVecsPerLane = TIDE_AG_U;
+constexpr int kWgPerCu = TIDE_WG_PER_CU;      // default grid: enough waves to keep HBM busy
+constexpr int kSmallFootprintWg = TIDE_SMALL_WG;  // small-footprint grid
 
 tide_status hip_fail(const char *what, hipError_t e) {
     return fail(TIDE_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -335,9 +444,24 @@ tide_status device_state(const tide_plan *p, DeviceState **out) {
     if (!ds) return fail(TIDE_E_NOMEM, "device state: out of host memory");
     ds->device = dev;
     e = hipDeviceGetAttribute(&ds->cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&ds->lds_per_cu,
+                                  hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&ds->lds_per_wg_max, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                                  dev);
     if (e != hipSuccess) {
         delete ds;
         return hip_fail("hipDeviceGetAttribute", e);
+    }
+    // A small-footprint workgroup reserves just over half of a CU's LDS, so
+    // no two of them share a CU: the hardware dispatcher has to spread them
+    // one per CU, and a CU that holds one cannot take two workgroups of an
+    // LDS-heavy kernel running beside it.  The reservation is never touched.
+    ds->small_lds = 0;
+    if (TIDE_SMALL_LDS_RESERVE && ds->lds_per_cu > 0) {
+        const int want = ds->lds_per_cu / 2 + 1024;
+        if (want <= ds->lds_per_wg_max) ds->small_lds = want;
     }
     tide_status st = upload(p->desc.data(), p->desc.size() * sizeof(ParamDesc), &ds->d_params,
                             "parameter table");
@@ -417,12 +541,33 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache,
     return TIDE_OK;
 }
 
+// Both launch modes give every tile its own short-lived workgroup, and the
+// hardware dispatcher balances them over all CUs.  Small-footprint launches
+// also reserve over half a CU's LDS per workgroup, so at most one of them
+// is resident on a CU at any moment: a concurrent GEMM keeps its place on
+// every CU and loses only a little issue bandwidth there.  max_wg > 0 caps
+// the grid (workgroups then loop over tiles).
 unsigned grid_size(const DeviceState *ds, int64_t ntiles, uint32_t flags, int32_t max_wg) {
-    int64_t g = (flags & TIDE_F_SMALL_FOOTPRINT) ? kSmallFootprintWg
-                                                 : static_cast<int64_t>(ds->cus) * kWgPerCu;
+    int64_t g;
+    if (flags & TIDE_F_SMALL_FOOTPRINT)
+        g = !TIDE_SMALL_PERSISTENT ? ntiles
+            : ds->small_lds        ? static_cast<int64_t>(ds->cus) * TIDE_SMALL_WG_PER_CU
+                                   : kSmallFootprintWg;
+    else if (TIDE_DEFAULT_ONE_TILE_PER_WG)
+        g = ntiles;
+    else
+        g = static_cast<int64_t>(ds->cus) * kWgPerCu;
     if (max_wg > 0) g = max_wg;
-    g = std::min(g, ntiles);
+    g = std::min<int64_t>({g, ntiles, 0x7fffffff});
     return static_cast<unsigned>(std::max<int64_t>(g, 1));
+}
+
+// Lets `kernel` launch with `bytes` of dynamic LDS (needed above 64 KiB).
+tide_status allow_lds(const void *kernel, int bytes) {
+    if (bytes <= 65536) return TIDE_OK;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return hip_fail("hipFuncSetAttribute (LDS reservation)", e);
+    return TIDE_OK;
 }
 
 }  // namespace
@@ -476,12 +621,22 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
     const int vec_in = pt->aligned16 ? 1 : 0;
     const int vec_out = (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(tide::rs_kernel<tide::kRsChunksPerLane>, dim3(grid), dim3(tide::kBlock), 0,
-                       static_cast<hipStream_t>(stream),
-                       static_cast<const tide::ParamDesc *>(ds->d_params),
-                       static_cast<const tide::Tile *>(ds->d_rs_tiles), ntiles,
-                       static_cast<const uint16_t *const *>(pt->dev), plan->N, rank, out, vec_in,
-                       vec_out);
+    const auto *pd = static_cast<const tide::ParamDesc *>(ds->d_params);
+    const auto *tl = static_cast<const tide::Tile *>(ds->d_rs_tiles);
+    const auto *gp = static_cast<const uint16_t *const *>(pt->dev);
+    if (flags & TIDE_F_SMALL_FOOTPRINT) {
+        auto k = tide::rs_kernel<TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_VEC, TIDE_SMALL_RB,
+                                 TIDE_SMALL_PACE, TIDE_XMAP_RS>;
+        st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->small_lds);
+        if (st != TIDE_OK) return st;
+        hipLaunchKernelGGL(k, dim3(grid), dim3(TIDE_SMALL_BLOCK), ds->small_lds,
+                           static_cast<hipStream_t>(stream), pd, tl, ntiles, gp, plan->N, rank,
+                           out, vec_in, vec_out);
+    } else
+        hipLaunchKernelGGL((tide::rs_kernel<tide::kBlock, tide::kRsChunksPerLane, TIDE_RS_VEC,
+                                            TIDE_RS_RB, 0, TIDE_XMAP_RS>),
+                           dim3(grid), dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream),
+                           pd, tl, ntiles, gp, plan->N, rank, out, vec_in, vec_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
     tide::clear_error();
@@ -516,11 +671,22 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
     const int64_t ntiles = static_cast<int64_t>(plan->ag_tiles.size());
     const unsigned grid = tide::grid_size(ds, ntiles, flags, max_workgroups);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(tide::ag_kernel<tide::kAgVecsPerLane>, dim3(grid), dim3(tide::kBlock), 0,
-                       static_cast<hipStream_t>(stream),
-                       static_cast<const tide::ParamDesc *>(ds->d_params),
-                       static_cast<const tide::Tile *>(ds->d_ag_tiles), ntiles,
-                       static_cast<const uintptr_t *>(pt->dev), plan->N, elem_bytes);
+    const auto *pd = static_cast<const tide::ParamDesc *>(ds->d_params);
+    const auto *tl = static_cast<const tide::Tile *>(ds->d_ag_tiles);
+    const auto *pp = static_cast<const uintptr_t *>(pt->dev);
+    if (flags & TIDE_F_SMALL_FOOTPRINT) {
+        auto k = tide::ag_kernel<TIDE_SMALL_BLOCK, tide::kAgVecsPerLane, TIDE_SMALL_PACE,
+                                 TIDE_XMAP_AG>;
+        st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->small_lds);
+        if (st != TIDE_OK) return st;
+        hipLaunchKernelGGL(k, dim3(grid), dim3(TIDE_SMALL_BLOCK), ds->small_lds,
+                           static_cast<hipStream_t>(stream), pd, tl, ntiles, pp, plan->N,
+                           elem_bytes);
+    } else
+        hipLaunchKernelGGL((tide::ag_kernel<tide::kBlock, tide::kAgVecsPerLane, 0, TIDE_XMAP_AG>),
+                           dim3(grid),
+                           dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream), pd, tl, ntiles,
+                           pp, plan->N, elem_bytes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return tide::hip_fail("tide_ag: kernel launch", e);
     tide::clear_error();
