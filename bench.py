@@ -20,6 +20,8 @@ Reported (one JSON line on stdout, progress on stderr):
   corun       slowdown of a bf16 8192^3 GEMM on another stream while
               tide_rs runs (default and small-footprint launch) on the
               64-rank 70B layer;
+  corun_ag    the same for tide_ag on the step's workload: kernel (default,
+              small footprint) and SDMA copy engine;
   cpu_baseline the CPU oracle on the same step's inputs (host cores).
 
 Algorithmic bytes (what the method must move; the fp32 pack buffer and the
@@ -51,6 +53,10 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama31_70b_layer.json
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fmt(x):
+    return "n/a" if x is None else f"{x:.2f}"
 
 
 def kernel_source_hash():
@@ -178,109 +184,156 @@ def counter_traffic(kernel):
 # co-run with a bf16 GEMM
 # ---------------------------------------------------------------------------
 
-def corun(w, gemm_shape, gemm_reps=30, modes=(False, True), repeats=2):
-    M, K, Nn = gemm_shape
+class Gemm:
+    """The co-running compute kernel: a bf16 GEMM on its own stream."""
+
+    def __init__(self, shape, reps=30):
+        M, K, Nn = shape
+        g = torch.Generator(device="cuda").manual_seed(77)
+        self.A = torch.randn(M, K, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        self.B = torch.randn(K, Nn, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        self.C = torch.empty(M, Nn, dtype=torch.bfloat16, device="cuda")
+        self.flop = 2.0 * M * K * Nn
+        self.name = f"bf16 {M}x{K}x{Nn} torch.matmul"
+        self.reps = reps
+        # Two streams for the whole co-run phase: the process has few hardware
+        # queues, and a stream created later can land on the GEMM's queue,
+        # which would serialise the two instead of running them together.
+        self.stream = torch.cuda.Stream()
+        self.side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        ev = timed_events(reps)
+        with torch.cuda.stream(self.stream):
+            for _ in range(5):
+                self.run()
+            for s, e in ev:
+                s.record()
+                self.run()
+                e.record()
+        torch.cuda.synchronize()
+        self.alone_ms = statistics.median(s.elapsed_time(e) for s, e in ev)
+
+    def run(self):
+        torch.matmul(self.A, self.B, out=self.C)
+
+
+def corun_chain(gemm, launch, nbytes, repeats=2):
+    """GEMMs on their stream while `launch(k, stream)` calls run back to back
+    on another stream (started first, long enough to cover every GEMM).
+    Returns the median GEMM slowdown over `repeats` runs and per-run detail;
+    only GEMMs that start and end inside the collective's window count."""
+    sb = gemm.side
+    ev = timed_events(6)
+    with torch.cuda.stream(sb):
+        for k in range(2):
+            launch(k, sb)
+        for k, (s, e) in enumerate(ev):
+            s.record()
+            launch(k, sb)
+            e.record()
+    torch.cuda.synchronize()
+    t_alone = statistics.median(s.elapsed_time(e) for s, e in ev)
+    runs = []
+    for _ in range(repeats):
+        n = int(1.5 * (gemm.reps + 4) * gemm.alone_ms / t_alone) + 4
+        base = torch.cuda.Event(enable_timing=True)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        first_done = torch.cuda.Event()
+        ev = timed_events(gemm.reps)
+        torch.cuda.synchronize()
+        base.record()
+        sb.wait_stream(torch.cuda.current_stream())
+        gemm.stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(sb):
+            c0.record()
+            launch(0, sb)
+            first_done.record()
+            for k in range(1, n):
+                launch(k, sb)
+            c1.record()
+        with torch.cuda.stream(gemm.stream):
+            gemm.stream.wait_event(first_done)
+            for _ in range(2):
+                gemm.run()
+            for s, e in ev:
+                s.record()
+                gemm.run()
+                e.record()
+        torch.cuda.synchronize()
+        lo, hi = base.elapsed_time(c0), base.elapsed_time(c1)
+        starts = [base.elapsed_time(s) for s, _ in ev]
+        ends = [base.elapsed_time(e) for _, e in ev]
+        inside = [e - s for s, e in zip(starts, ends) if s >= lo and e <= hi]
+        if len(inside) < gemm.reps // 2:
+            log(f"co-run: only {len(inside)} of {gemm.reps} GEMMs ran inside the collective's "
+                f"window {lo:.1f}-{hi:.1f} ms (GEMMs {min(starts):.1f}-{max(ends):.1f} ms); "
+                "this run does not measure concurrency")
+            inside = []
+        med = statistics.median(inside) if inside else None
+        runs.append({
+            "gemm_corun_ms": med,
+            "gemms_fully_overlapped": len(inside),
+            "gemm_slowdown_pct": None if med is None else 100.0 * (med / gemm.alone_ms - 1.0),
+            "corun_GBps": n * nbytes / ((hi - lo) * 1e-3) / 1e9,
+            "calls": n,
+            "window_ms": [lo, hi],
+            "gemms_ms": [min(starts), max(ends)],
+        })
+    slow = [r["gemm_slowdown_pct"] for r in runs if r["gemm_slowdown_pct"] is not None]
+    return {
+        "alone_us": t_alone * 1e3,
+        "alone_GBps": nbytes / (t_alone * 1e-3) / 1e9,
+        "corun_GBps": statistics.median(r["corun_GBps"] for r in runs),
+        "gemm_slowdown_pct": statistics.median(slow) if slow else None,
+        "runs": runs,
+    }
+
+
+CORUN_METHOD = ("stream A runs the GEMMs, stream B a chain of collective calls started first and "
+                "long enough to cover them; slowdown = median GEMM time while the chain runs / "
+                "median GEMM time alone - 1, counting only GEMMs that start and end inside the "
+                "chain's window; median of 2 runs")
+
+
+def corun_rs(w, gemm):
+    """tide_rs beside the GEMM, default and small-footprint launch."""
     N = w.world
-    log(f"co-run: generating {w.name} ({N} ranks) and a bf16 {M}x{K}x{Nn} GEMM")
+    log(f"co-run: generating {w.name} ({N} ranks) beside a {gemm.name}")
     grads = workloads.all_grads(w, device="cuda")
     plan = tide.Plan(w.shapes, N)
     table = tide.grad_table(plan, grads)
     out = torch.empty(N, plan.S, dtype=torch.float32, device="cuda")
-    g = torch.Generator(device="cuda").manual_seed(77)
-    A = torch.randn(M, K, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-    B = torch.randn(K, Nn, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-    C = torch.empty(M, Nn, dtype=torch.bfloat16, device="cuda")
-    sa = torch.cuda.Stream()
-    sb = torch.cuda.Stream()
     b_rs = rs_bytes(plan, 0)
-    torch.cuda.synchronize()
-
-    def gemm_alone():
-        ev = timed_events(gemm_reps)
-        with torch.cuda.stream(sa):
-            for _ in range(5):
-                torch.matmul(A, B, out=C)
-            for s, e in ev:
-                s.record()
-                torch.matmul(A, B, out=C)
-                e.record()
-        torch.cuda.synchronize()
-        return [s.elapsed_time(e) for s, e in ev]
-
-    def rs_alone(small, reps=10):
-        ev = timed_events(reps)
-        with torch.cuda.stream(sb):
-            for k in range(3):
-                tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
-            for k, (s, e) in enumerate(ev):
-                s.record()
-                tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
-                e.record()
-        torch.cuda.synchronize()
-        return statistics.median(s.elapsed_time(e) for s, e in ev)
-
-    alone = gemm_alone()
-    t_gemm = statistics.median(alone)
-    res = {"gemm": f"bf16 {M}x{K}x{Nn} torch.matmul", "gemm_alone_ms": t_gemm,
-           "gemm_tflops_alone": 2.0 * M * K * Nn / (t_gemm * 1e-3) / 1e12,
-           "workload": w.name, "world": N, "repeats": repeats,
-           "method": ("stream A runs the GEMMs, stream B a chain of tide_rs calls (rank "
-                      "rotating) started first and long enough to cover them; slowdown = "
-                      "median GEMM time while tide_rs runs / median GEMM time alone - 1, "
-                      "counting only GEMMs that start and end inside the tide_rs window")}
-    for small in modes:
-        t_rs = rs_alone(small)
+    res = {"gemm": gemm.name, "gemm_alone_ms": gemm.alone_ms,
+           "gemm_tflops_alone": gemm.flop / (gemm.alone_ms * 1e-3) / 1e12,
+           "workload": w.name, "world": N, "method": CORUN_METHOD}
+    for small in (False, True):
         key = "small_footprint" if small else "default"
-        runs = []
-        for _ in range(repeats):
-            n_rs = int(1.5 * (gemm_reps + 4) * t_gemm / t_rs) + 4
-            base = torch.cuda.Event(enable_timing=True)
-            rs_start = torch.cuda.Event(enable_timing=True)
-            rs_end = torch.cuda.Event(enable_timing=True)
-            first_done = torch.cuda.Event()
-            ev = timed_events(gemm_reps)
-            torch.cuda.synchronize()
-            base.record()
-            sb.wait_stream(torch.cuda.current_stream())
-            sa.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(sb):
-                rs_start.record()
-                tide.rs(plan, 0, table, out[0], small=small, stream=sb)
-                first_done.record()
-                for k in range(1, n_rs):
-                    tide.rs(plan, k % N, table, out[k % N], small=small, stream=sb)
-                rs_end.record()
-            with torch.cuda.stream(sa):
-                sa.wait_event(first_done)
-                for _ in range(2):
-                    torch.matmul(A, B, out=C)
-                for s, e in ev:
-                    s.record()
-                    torch.matmul(A, B, out=C)
-                    e.record()
-            torch.cuda.synchronize()
-            rs_lo = base.elapsed_time(rs_start)
-            rs_hi = base.elapsed_time(rs_end)
-            inside = [s.elapsed_time(e) for s, e in ev
-                      if base.elapsed_time(s) >= rs_lo and base.elapsed_time(e) <= rs_hi]
-            med = statistics.median(inside) if inside else None
-            runs.append({
-                "gemm_corun_ms": med,
-                "gemms_fully_overlapped": len(inside),
-                "gemm_slowdown_pct": None if med is None else 100.0 * (med / t_gemm - 1.0),
-                "tide_rs_corun_GBps": n_rs * b_rs / ((rs_hi - rs_lo) * 1e-3) / 1e9,
-            })
-        slow = [r["gemm_slowdown_pct"] for r in runs if r["gemm_slowdown_pct"] is not None]
-        res[key] = {
-            "tide_rs_alone_us": t_rs * 1e3,
-            "tide_rs_alone_GBps": b_rs / (t_rs * 1e-3) / 1e9,
-            "tide_rs_corun_GBps": statistics.median(r["tide_rs_corun_GBps"] for r in runs),
-            "gemm_slowdown_pct": statistics.median(slow) if slow else None,
-            "runs": runs,
-        }
-        log(f"co-run {key}: slowdown {res[key]['gemm_slowdown_pct']:.2f}% "
-            f"(runs {[round(x, 2) for x in slow]}), tide_rs {res[key]['tide_rs_corun_GBps']:.0f} GB/s")
-    del grads, table, out, A, B, C
+        r = corun_chain(gemm, lambda k, st: tide.rs(plan, k % N, table, out[k % N], small=small,
+                                                     stream=st), b_rs)
+        res[key] = {"tide_rs_alone_us": r["alone_us"], "tide_rs_alone_GBps": r["alone_GBps"],
+                    "tide_rs_corun_GBps": r["corun_GBps"],
+                    "gemm_slowdown_pct": r["gemm_slowdown_pct"], "runs": r["runs"]}
+        log(f"co-run tide_rs {key}: slowdown {fmt(r['gemm_slowdown_pct'])}% runs {r['runs']}, "
+            f"{r['corun_GBps']:.0f} GB/s during, {r['alone_GBps']:.0f} GB/s alone")
+    del grads, table, out
+    return res
+
+
+def corun_ag(step, gemm):
+    """tide_ag beside the GEMM: kernel (default, small footprint) and SDMA copy engine."""
+    res = {"gemm": gemm.name, "gemm_alone_ms": gemm.alone_ms, "workload": step.w.name,
+           "world": step.w.world, "method": CORUN_METHOD}
+    for key, kw in (("default", {}), ("small_footprint", {"small": True}),
+                    ("copy_engine", {"copy_engine": True})):
+        r = corun_chain(gemm, lambda k, st: tide.ag(step.plan, None, None, stream=st,
+                                                     tables=step.agt, **kw), step.b_ag)
+        res[key] = {"tide_ag_alone_us": r["alone_us"], "tide_ag_alone_GBps": r["alone_GBps"],
+                    "tide_ag_corun_GBps": r["corun_GBps"],
+                    "gemm_slowdown_pct": r["gemm_slowdown_pct"], "runs": r["runs"]}
+        log(f"co-run tide_ag {key}: slowdown {fmt(r['gemm_slowdown_pct'])}% runs {r['runs']}, "
+            f"{r['corun_GBps']:.0f} GB/s during, {r['alone_GBps']:.0f} GB/s alone")
     return res
 
 
@@ -397,14 +450,18 @@ def main():
     if copy_gbps:
         log(f"copy ceiling {copy_gbps:.1f} GB/s")
     cpu = None if args.no_cpu else cpu_baseline(step)
+    corun_res = corun_ag_res = None
+    gemm = None
+    if args.corun != "none":
+        cw = workloads.WORKLOADS[args.corun]
+        gemm = Gemm(cw.corun_gemm or (8192, 8192, 8192))
+        corun_ag_res = corun_ag(step, gemm)
     P, S = step.plan.P, step.plan.S
     del step
     gc.collect()
     torch.cuda.empty_cache()
-    corun_res = None
-    if args.corun != "none":
-        cw = workloads.WORKLOADS[args.corun]
-        corun_res = corun(cw, cw.corun_gemm or (8192, 8192, 8192))
+    if gemm is not None:
+        corun_res = corun_rs(cw, gemm)
         gc.collect()
         torch.cuda.empty_cache()
 
@@ -440,6 +497,7 @@ def main():
         "tide_rs": rs_k,
         "tide_ag": ag_k,
         "corun": corun_res,
+        "corun_ag": corun_ag_res,
         "gemm_slowdown_pct": None if not corun_res else {
             k: corun_res[k]["gemm_slowdown_pct"] for k in ("default", "small_footprint")
             if k in corun_res},

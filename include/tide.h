@@ -69,12 +69,24 @@ typedef enum tide_status {
 /* Opaque plan: the shard geometry of one parameter list for one world size. */
 typedef struct tide_plan tide_plan;
 
-/* Launch flag: small-footprint mode.  Caps the number of workgroups so that
- * a compute kernel on another stream (a bf16 GEMM) keeps most of the chip.
- * The pages trace interference to collectives that occupy the compute units
- * a concurrent GEMM needs (TIDE article, §"FSDP2通信开销的根源"), and TIDE's
- * answer is to keep collectives off them (§"TIDE的设计思路"). */
+/* Launch flag: small-footprint mode, for running beside a compute kernel on
+ * another stream (e.g. a bf16 GEMM).  Every tile still gets a short-lived
+ * workgroup, but each one reserves just over half of a compute unit's LDS,
+ * so at most one is resident per compute unit at any moment and the other
+ * kernel keeps its place on every unit.  The pages trace the interference to
+ * collectives that occupy the compute units a concurrent GEMM needs (TIDE
+ * article, §"FSDP2通信开销的根源"); TIDE's answer is to keep collectives off
+ * them, with copy engines and short-lived thread blocks (§"TIDE的设计思路"). */
 #define TIDE_F_SMALL_FOOTPRINT 0x1u
+
+/* Launch flag, tide_ag only: place the shards with the SDMA copy engines
+ * (hipMemcpyDeviceToDeviceNoCU copies) and no kernel at all, so a concurrent
+ * compute kernel keeps every compute unit.  This is the analogue of TIDE-AG
+ * moving data without occupying SMs (TIDE article, §"TIDE的设计思路").  One
+ * 2-D copy per parameter covers the ranks that hold full shards when the N
+ * rank blocks are equally spaced; otherwise one copy per (parameter, rank).
+ * tide_rs rejects it with TIDE_E_UNSUPPORTED: a reduction needs arithmetic. */
+#define TIDE_F_COPY_ENGINE 0x2u
 
 /* ---------------------------------------------------------------------- */
 /* Plan (host only; makes no HIP call).                                    */
@@ -151,8 +163,13 @@ tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *const *grad
  *   params      host array of P device pointers to the full tensors
  *               (dim0_i*inner_i elements; NULL allowed when that is 0).
  *   elem_bytes  2 (bf16/fp16) or 4 (fp32).
- *   flags, max_workgroups, stream  as for tide_rs.
- * Destinations must not overlap one another or any element that is read. */
+ *   flags       0, TIDE_F_SMALL_FOOTPRINT or TIDE_F_COPY_ENGINE (not both);
+ *               other bits -> TIDE_E_UNSUPPORTED.
+ *   max_workgroups, stream  as for tide_rs (max_workgroups is ignored with
+ *               TIDE_F_COPY_ENGINE).
+ * Destinations must not overlap one another or any element that is read.
+ * With TIDE_F_COPY_ENGINE the call enqueues several copies; if the runtime
+ * rejects one of them (TIDE_E_HIP), copies enqueued before it still run. */
 tide_status tide_ag(const tide_plan *plan, const void *const *rank_src,
                     void *const *params, int32_t elem_bytes, uint32_t flags,
                     int32_t max_workgroups, void *stream);

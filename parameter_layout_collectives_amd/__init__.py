@@ -17,6 +17,7 @@ import torch
 from ._lib import lib
 
 SMALL_FOOTPRINT = 0x1
+COPY_ENGINE = 0x2
 
 _STATUS = {0: "TIDE_OK", 1: "TIDE_E_INVALID", 2: "TIDE_E_UNSUPPORTED", 3: "TIDE_E_NOMEM",
            4: "TIDE_E_HIP"}
@@ -176,17 +177,20 @@ def ag_tables(plan, rank_src, params):
     return PointerTable(blocks), PointerTable(params), _ELEM[dt]
 
 
-def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, tables=None):
+def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, tables=None,
+       copy_engine=False):
     """TIDE-AG placement: scatter N rank blocks into full parameter tensors.
 
     rank_src: one contiguous N*S buffer (rank-major) or a list of N blocks.
     params: list of P full tensors of the same dtype (2- or 4-byte elements).
-    tables: optional result of ag_tables() to skip re-marshalling."""
+    tables: optional result of ag_tables() to skip re-marshalling.
+    copy_engine: place the shards with SDMA copies instead of a kernel."""
     src_t, dst_t, e = tables if tables is not None else ag_tables(plan, rank_src, params)
-    _check(lib().tide_ag(plan.handle, src_t.array, dst_t.array, e,
-                         SMALL_FOOTPRINT if small else 0, int(max_workgroups),
+    flags = (SMALL_FOOTPRINT if small else 0) | (COPY_ENGINE if copy_engine else 0)
+    _check(lib().tide_ag(plan.handle, src_t.array, dst_t.array, e, flags, int(max_workgroups),
                          _stream_handle(stream)))
 
 
-__all__ = ["Plan", "PointerTable", "TideError", "SMALL_FOOTPRINT", "grad_table", "ag_tables",
+__all__ = ["Plan", "PointerTable", "TideError", "SMALL_FOOTPRINT", "COPY_ENGINE", "grad_table",
+           "ag_tables",
            "rs", "ag", "lib"]

@@ -21,14 +21,21 @@ namespace tide {
 #ifndef TIDE_AG_TILE
 #define TIDE_AG_TILE 2048
 #endif
+#ifndef TIDE_AG_TILE_SMALL
+#define TIDE_AG_TILE_SMALL 16384
+#endif
 
 // Elements of one parameter segment handled by one reduce-scatter tile, and
 // by one all-gather tile.  Both are multiples of 8 so that tile starts keep
 // the 16-byte phase of the segment they cut.
 constexpr int64_t kRsTile = TIDE_RS_TILE;
 constexpr int64_t kAgTile = TIDE_AG_TILE;
-static_assert(kRsTile % 8 == 0 && kAgTile % 8 == 0, "tiles must keep the 16-byte phase");
-static_assert(kAgTile * 4 < (int64_t(1) << 31), "all-gather tile bytes must fit in int");
+// Small-footprint all-gather launches keep one workgroup per CU resident, so
+// each one moves a larger tile to keep enough bytes in flight.
+constexpr int64_t kAgTileSmall = TIDE_AG_TILE_SMALL;
+static_assert(kRsTile % 8 == 0 && kAgTile % 8 == 0 && kAgTileSmall % 8 == 0,
+              "tiles must keep the 16-byte phase");
+static_assert(kAgTileSmall * 4 < (int64_t(1) << 31), "all-gather tile bytes must fit in int");
 constexpr int kBlock = 256;           // lanes per workgroup (4 wave64)
 
 // Per-parameter geometry as the kernels read it.  src(r) = r*seg and
@@ -66,6 +73,7 @@ struct DeviceState {
     void *d_params = nullptr;    // ParamDesc[P]
     void *d_rs_tiles = nullptr;  // Tile[n_rs]
     void *d_ag_tiles = nullptr;  // Tile[n_ag]
+    void *d_ag_tiles_small = nullptr;  // Tile[n_ag_small]
     std::vector<PtrTable> rs_cache, ag_cache;
     uint64_t tick = 0;
 };
@@ -79,7 +87,7 @@ struct tide_plan {
     int64_t align = 1, S = 0, psi = 0;
     std::vector<int64_t> d0, inner, c, seg, off, numel;
     std::vector<tide::ParamDesc> desc;
-    std::vector<tide::Tile> rs_tiles, ag_tiles;
+    std::vector<tide::Tile> rs_tiles, ag_tiles, ag_tiles_small;
     mutable std::mutex mu;
     mutable std::vector<tide::DeviceState *> devs;
 };

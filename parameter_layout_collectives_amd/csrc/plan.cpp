@@ -68,6 +68,9 @@ tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *g
     if (rank < 0 || rank >= p->N)
         return fail(TIDE_E_INVALID, "tide_rs: rank " + std::to_string(rank) +
                                         " outside [0, " + std::to_string(p->N) + ")");
+    if (flags & TIDE_F_COPY_ENGINE)
+        return fail(TIDE_E_UNSUPPORTED,
+                    "tide_rs: TIDE_F_COPY_ENGINE is for tide_ag (a reduction needs arithmetic)");
     if (flags & ~TIDE_F_SMALL_FOOTPRINT)
         return fail(TIDE_E_UNSUPPORTED, "tide_rs: unknown flag bits");
     if (max_wg < 0) return fail(TIDE_E_INVALID, "tide_rs: max_workgroups < 0");
@@ -108,8 +111,11 @@ tide_status check_ag_args(const tide_plan *p, const void *const *rank_src,
     if (!p) return fail(TIDE_E_INVALID, "tide_ag: plan is NULL");
     if (elem_bytes != 2 && elem_bytes != 4)
         return fail(TIDE_E_INVALID, "tide_ag: elem_bytes must be 2 or 4");
-    if (flags & ~TIDE_F_SMALL_FOOTPRINT)
+    if (flags & ~(TIDE_F_SMALL_FOOTPRINT | TIDE_F_COPY_ENGINE))
         return fail(TIDE_E_UNSUPPORTED, "tide_ag: unknown flag bits");
+    if ((flags & TIDE_F_SMALL_FOOTPRINT) && (flags & TIDE_F_COPY_ENGINE))
+        return fail(TIDE_E_UNSUPPORTED,
+                    "tide_ag: TIDE_F_SMALL_FOOTPRINT and TIDE_F_COPY_ENGINE exclude each other");
     if (max_wg < 0) return fail(TIDE_E_INVALID, "tide_ag: max_workgroups < 0");
     if (p->psi == 0) return TIDE_OK;
     if (!rank_src) return fail(TIDE_E_INVALID, "tide_ag: rank_src array is NULL");
@@ -229,6 +235,8 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int64_t *dim0
                 int64_t src, L;
                 tide::shard_run(p, r, i, &src, &L);
                 for (int64_t k = 0; k < L; k += tide::kAgTile) p->ag_tiles.push_back({i, r, k});
+                for (int64_t k = 0; k < L; k += tide::kAgTileSmall)
+                    p->ag_tiles_small.push_back({i, r, k});
             }
     } catch (const std::bad_alloc &) {
         delete p;

@@ -277,7 +277,8 @@ __device__ __forceinline__ void copy_elems(const char *s, char *d, int a, int b,
 // Copies n bytes from s to d where s = d (mod W): element-wise up to the
 // first W-aligned destination byte, W-byte vectors (U per lane in flight),
 // element-wise tail.
-// n is at most kAgTile * 4 bytes, so lane offsets fit in 32 bits.
+// n is at most one all-gather tile of 4-byte elements, so lane offsets fit in
+// 32 bits.
 template <int BLOCK, int W, int U>
 __device__ __forceinline__ void copy_span_w(const char *s, char *d, int n, int e) {
     typedef typename VecOf<W>::type V;
@@ -303,10 +304,10 @@ __device__ __forceinline__ void copy_span_w(const char *s, char *d, int n, int e
     copy_elems<BLOCK>(s, d, h + nv * W, n, e);
 }
 
-// Tile t covers elements [k0, k0 + kAgTile) of rank r's shard of parameter
+// Tile t covers elements [k0, k0 + TILE) of rank r's shard of parameter
 // i: they move from rank_src[r] + off_i + k to params[i] + r*seg_i + k.
 // ptrs = rank_src[0..N) followed by params[0..P).
-template <int BLOCK, int U, int PACE, bool XMAP>
+template <int BLOCK, int U, int PACE, bool XMAP, int64_t TILE>
 __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__ pdesc,
                                                     const Tile *__restrict__ tiles,
                                                     int64_t ntiles,
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
         const int64_t src = static_cast<int64_t>(tile.rank) * d.seg;
         int64_t L = d.numel - src;
         L = L < 0 ? 0 : (L > d.seg ? d.seg : L);
-        const int64_t len = min(kAgTile, L - tile.k0);
+        const int64_t len = min(TILE, L - tile.k0);
         const char *s = reinterpret_cast<const char *>(ptrs[tile.rank]) + (d.off + tile.k0) * e;
         char *dst = reinterpret_cast<char *>(ptrs[N + tile.param]) + (src + tile.k0) * e;
         const int n = static_cast<int>(len * e);
@@ -381,6 +382,9 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
 #ifndef TIDE_XMAP_RS
 #define TIDE_XMAP_RS 0
 #endif
+#ifndef TIDE_SMALL_AG_U
+#define TIDE_SMALL_AG_U 8
+#endif
 #ifndef TIDE_XMAP_AG
 #define TIDE_XMAP_AG 1
 #endif
@@ -424,6 +428,7 @@ void free_state(DeviceState *ds) {
     (void)hipFree(ds->d_params);
     (void)hipFree(ds->d_rs_tiles);
     (void)hipFree(ds->d_ag_tiles);
+    (void)hipFree(ds->d_ag_tiles_small);
     for (auto &pt : ds->rs_cache) (void)hipFree(pt.dev);
     for (auto &pt : ds->ag_cache) (void)hipFree(pt.dev);
     delete ds;
@@ -471,6 +476,9 @@ tide_status device_state(const tide_plan *p, DeviceState **out) {
     if (st == TIDE_OK)
         st = upload(p->ag_tiles.data(), p->ag_tiles.size() * sizeof(Tile), &ds->d_ag_tiles,
                     "all-gather tiles");
+    if (st == TIDE_OK)
+        st = upload(p->ag_tiles_small.data(), p->ag_tiles_small.size() * sizeof(Tile),
+                    &ds->d_ag_tiles_small, "all-gather tiles (small footprint)");
     if (st != TIDE_OK) {
         free_state(ds);
         return st;
@@ -643,6 +651,68 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
     return TIDE_OK;
 }
 
+namespace tide {
+namespace {
+
+// TIDE-AG placement with the SDMA engines: the same (parameter, rank) runs as
+// the kernel copies, as device-to-device copies that use no compute unit.
+// The ranks holding a full shard of parameter i form a prefix 0..F-1; when
+// the rank blocks are equally spaced (one gathered buffer) those F runs are
+// one 2-D copy: F rows of seg_i elements, source pitch = block spacing,
+// destination pitch = seg_i.  The one short rank (if any) is a 1-D copy.
+tide_status ag_copy_engine(const tide_plan *p, const void *const *rank_src, void *const *params,
+                           int32_t e, hipStream_t stream) {
+    const hipMemcpyKind kind = hipMemcpyDeviceToDeviceNoCU;
+    const uintptr_t eb = static_cast<uintptr_t>(e);
+    bool equal = p->N > 1;
+    uintptr_t pitch = 0;
+    if (equal) {
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(rank_src[0]);
+        const uintptr_t b1 = reinterpret_cast<uintptr_t>(rank_src[1]);
+        equal = b1 > b0;
+        pitch = b1 - b0;
+        for (int32_t r = 2; equal && r < p->N; r++)
+            equal = reinterpret_cast<uintptr_t>(rank_src[r]) ==
+                    reinterpret_cast<uintptr_t>(rank_src[r - 1]) + pitch;
+    }
+    for (int32_t i = 0; i < p->P; i++) {
+        if (p->numel[i] == 0 || p->seg[i] == 0) continue;
+        const uintptr_t seg_b = static_cast<uintptr_t>(p->seg[i]) * eb;
+        const uintptr_t off_b = static_cast<uintptr_t>(p->off[i]) * eb;
+        char *dst = static_cast<char *>(params[i]);
+        int32_t full = 0;
+        while (full < p->N) {
+            int64_t src, L;
+            shard_run(p, full, i, &src, &L);
+            if (L != p->seg[i]) break;
+            full++;
+        }
+        hipError_t err = hipSuccess;
+        if (equal && full > 1 && pitch >= seg_b) {
+            err = hipMemcpy2DAsync(dst, seg_b, static_cast<const char *>(rank_src[0]) + off_b,
+                                   pitch, seg_b, static_cast<size_t>(full), kind, stream);
+        } else {
+            for (int32_t r = 0; r < full && err == hipSuccess; r++)
+                err = hipMemcpyAsync(dst + static_cast<uintptr_t>(r) * seg_b,
+                                     static_cast<const char *>(rank_src[r]) + off_b, seg_b, kind,
+                                     stream);
+        }
+        if (err == hipSuccess && full < p->N) {
+            int64_t src, L;
+            shard_run(p, full, i, &src, &L);
+            if (L > 0)
+                err = hipMemcpyAsync(dst + static_cast<uintptr_t>(src) * eb,
+                                     static_cast<const char *>(rank_src[full]) + off_b,
+                                     static_cast<uintptr_t>(L) * eb, kind, stream);
+        }
+        if (err != hipSuccess) return hip_fail("tide_ag: copy-engine copy", err);
+    }
+    return TIDE_OK;
+}
+
+}  // namespace
+}  // namespace tide
+
 extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_src,
                                void *const *params, int32_t elem_bytes, uint32_t flags,
                                int32_t max_workgroups, void *stream) {
@@ -650,6 +720,12 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
         tide::check_ag_args(plan, rank_src, params, elem_bytes, flags, max_workgroups);
     if (st != TIDE_OK) return st;
     if (plan->ag_tiles.empty()) return TIDE_OK;
+    if (flags & TIDE_F_COPY_ENGINE) {
+        st = tide::ag_copy_engine(plan, rank_src, params, elem_bytes,
+                                  static_cast<hipStream_t>(stream));
+        if (st == TIDE_OK) tide::clear_error();
+        return st;
+    }
 
     std::vector<uintptr_t> key;
     try {
@@ -668,25 +744,29 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
     st = tide::pointer_table(ds, ds->ag_cache, key, key, &pt);
     if (st != TIDE_OK) return st;
 
-    const int64_t ntiles = static_cast<int64_t>(plan->ag_tiles.size());
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    const int64_t ntiles =
+        static_cast<int64_t>(small ? plan->ag_tiles_small.size() : plan->ag_tiles.size());
     const unsigned grid = tide::grid_size(ds, ntiles, flags, max_workgroups);
     (void)hipGetLastError();
     const auto *pd = static_cast<const tide::ParamDesc *>(ds->d_params);
-    const auto *tl = static_cast<const tide::Tile *>(ds->d_ag_tiles);
     const auto *pp = static_cast<const uintptr_t *>(pt->dev);
-    if (flags & TIDE_F_SMALL_FOOTPRINT) {
-        auto k = tide::ag_kernel<TIDE_SMALL_BLOCK, tide::kAgVecsPerLane, TIDE_SMALL_PACE,
-                                 TIDE_XMAP_AG>;
+    if (small) {
+        auto k = tide::ag_kernel<TIDE_SMALL_BLOCK, TIDE_SMALL_AG_U, TIDE_SMALL_PACE, TIDE_XMAP_AG,
+                                 tide::kAgTileSmall>;
         st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->small_lds);
         if (st != TIDE_OK) return st;
         hipLaunchKernelGGL(k, dim3(grid), dim3(TIDE_SMALL_BLOCK), ds->small_lds,
-                           static_cast<hipStream_t>(stream), pd, tl, ntiles, pp, plan->N,
+                           static_cast<hipStream_t>(stream), pd,
+                           static_cast<const tide::Tile *>(ds->d_ag_tiles_small), ntiles, pp,
+                           plan->N, elem_bytes);
+    } else {
+        hipLaunchKernelGGL((tide::ag_kernel<tide::kBlock, tide::kAgVecsPerLane, 0, TIDE_XMAP_AG,
+                                            tide::kAgTile>),
+                           dim3(grid), dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream), pd,
+                           static_cast<const tide::Tile *>(ds->d_ag_tiles), ntiles, pp, plan->N,
                            elem_bytes);
-    } else
-        hipLaunchKernelGGL((tide::ag_kernel<tide::kBlock, tide::kAgVecsPerLane, 0, TIDE_XMAP_AG>),
-                           dim3(grid),
-                           dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream), pd, tl, ntiles,
-                           pp, plan->N, elem_bytes);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return tide::hip_fail("tide_ag: kernel launch", e);
     tide::clear_error();

@@ -125,7 +125,9 @@ def test_rs_argument_errors():
     assert _rs(None, 0, good, out) == E_INVALID
     assert _rs(plan, 2, good, out) == E_INVALID and b"rank" in L.tide_last_error()
     assert _rs(plan, -1, good, out) == E_INVALID
-    assert _rs(plan, 0, good, out, flags=0x2) == E_UNSUPPORTED
+    assert _rs(plan, 0, good, out, flags=0x2) == E_UNSUPPORTED   # copy engine: AG only
+    assert b"tide_ag" in L.tide_last_error()
+    assert _rs(plan, 0, good, out, flags=0x4) == E_UNSUPPORTED
     assert _rs(plan, 0, good, out, max_wg=-1) == E_INVALID
     assert _rs(plan, 0, None, out) == E_INVALID and b"grads" in L.tide_last_error()
     assert _rs(plan, 0, good, 0) == E_INVALID and b"out is NULL" in L.tide_last_error()
@@ -156,6 +158,8 @@ def test_ag_argument_errors():
     assert _ag(None, srcs, dsts) == E_INVALID
     assert _ag(plan, srcs, dsts, e=3) == E_INVALID and b"elem_bytes" in L.tide_last_error()
     assert _ag(plan, srcs, dsts, flags=0x8) == E_UNSUPPORTED
+    assert _ag(plan, srcs, dsts, flags=0x3) == E_UNSUPPORTED   # small + copy engine
+    assert b"exclude" in L.tide_last_error()
     assert _ag(plan, srcs, dsts, max_wg=-5) == E_INVALID
     assert _ag(plan, None, dsts) == E_INVALID
     assert _ag(plan, srcs, None) == E_INVALID

@@ -58,17 +58,19 @@ def _rs_cases(orc, w, grads, plan, table, ranks, modes):
 def _ag_case(orc, w, plan):
     N, S = w.world, plan.S
     gathered = workloads.random_bf16(N * S, seed=4242, sigma=w.sigma, device=DEV)
-    params = [torch.full(s, 0, dtype=torch.int16, device=DEV).fill_(BF16_SENTINEL)
-              .view(torch.bfloat16) for s in w.shapes]
-    note(f"{w.name}: tide_ag N={N} S={S}")
-    tide.ag(plan, gathered, params)
-    torch.cuda.synchronize()
     host = bits16(gathered)
     want = orc.ag(w.shapes, N, [host[r * S:(r + 1) * S] for r in range(N)], elem_bytes=2)
-    for i, p in enumerate(params):
-        got = bits16(p).reshape(-1)
-        bad = np.nonzero(got != want[i])[0]
-        assert bad.size == 0, (w.name, i, int(bad[0]) if bad.size else None, bad.size)
+    for kw in ({}, {"small": True}, {"copy_engine": True}):
+        params = [torch.full(s, 0, dtype=torch.int16, device=DEV).fill_(BF16_SENTINEL)
+                  .view(torch.bfloat16) for s in w.shapes]
+        note(f"{w.name}: tide_ag N={N} S={S} {kw}")
+        tide.ag(plan, gathered, params, **kw)
+        torch.cuda.synchronize()
+        for i, p in enumerate(params):
+            got = bits16(p).reshape(-1)
+            bad = np.nonzero(got != want[i])[0]
+            assert bad.size == 0, (w.name, kw, i, int(bad[0]) if bad.size else None, bad.size)
+        del params
 
 
 @pytest.mark.timeout(900)

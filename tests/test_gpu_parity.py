@@ -235,7 +235,7 @@ def check_ag(orc, shapes, N, e=2, align=1, src_shift=0, dst_shift=0, **kw):
 
 def test_ag_tiny(orc):
     w = workloads.WORKLOADS["tiny"]
-    for kw in ({}, {"small": True}, {"max_workgroups": 1}):
+    for kw in ({}, {"small": True}, {"max_workgroups": 1}, {"copy_engine": True}):
         check_ag(orc, w.shapes, w.world, **kw)
 
 
@@ -244,6 +244,35 @@ def test_ag_tiny(orc):
 def test_ag_ragged(orc, N, e):
     check_ag(orc, RAGGED[0], N, e=e)
     check_ag(orc, RAGGED[1], N, e=e, align=8)
+    check_ag(orc, RAGGED[0], N, e=e, small=True)
+
+
+@pytest.mark.parametrize("N", [1, 2, 5, 16])
+@pytest.mark.parametrize("e", [2, 4])
+def test_ag_copy_engine(orc, N, e):
+    """SDMA placement: 2-D copies over the full ranks, 1-D for the short rank."""
+    check_ag(orc, RAGGED[0], N, e=e, copy_engine=True)
+    check_ag(orc, RAGGED[1], N, e=e, align=8, copy_engine=True)
+    check_ag(orc, [(1031, 3), (9000,), (5, 5)], N, e=e, src_shift=1, dst_shift=3,
+             copy_engine=True)
+
+
+def test_ag_copy_engine_separate_blocks(orc):
+    """Rank blocks in separate allocations (not equally spaced): one copy per
+    (parameter, rank)."""
+    shapes = [(37, 3), (4100,), (2, 2)]
+    N = 5
+    plan = tide.Plan(shapes, N)
+    rng = np.random.default_rng(12)
+    host = [rng.integers(0, 65535, size=plan.S).astype(np.uint16) for _ in range(N)]
+    blocks = [torch.from_numpy(h.view(np.int16)).to(DEV).view(torch.bfloat16) for h in host]
+    params = [torch.full(s, 0, dtype=torch.int16, device=DEV).fill_(BF16_SENTINEL)
+              .view(torch.bfloat16) for s in shapes]
+    tide.ag(plan, blocks, params, copy_engine=True)
+    torch.cuda.synchronize()
+    want = orc.ag(shapes, N, host, elem_bytes=2)
+    for i, p in enumerate(params):
+        assert np.array_equal(bits16(p).reshape(-1), want[i]), i
 
 
 @pytest.mark.parametrize("src_shift,dst_shift", [(1, 0), (0, 3), (5, 5), (2, 6), (4, 0)])
@@ -271,3 +300,60 @@ def test_ag_inverts_rs_layout(orc):
     want = orc.ag(shapes, N, want_blocks, elem_bytes=4)
     for i in range(len(shapes)):
         assert np.array_equal(bits32(params[i]).reshape(-1), want[i]), i
+
+
+# ---------------------------------------------------------------------------
+# runtime behaviour
+# ---------------------------------------------------------------------------
+
+def test_pointer_table_cache_eviction(orc):
+    """More gradient sets than the plan caches (8): tables are evicted and
+    re-uploaded, and every call still reads the right tensors."""
+    shapes = [(33, 5), (4100,)]
+    N = 3
+    plan = tide.Plan(shapes, N)
+    sets = [to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=1000 + 10 * j))
+            for j in range(11)]
+    out = fresh_out(plan.S)
+    for sweep in range(2):
+        for j, g in enumerate(sets):
+            R = (j + sweep) % N
+            note(f"cache eviction: set {j} R={R} sweep {sweep}")
+            run_rs(plan, R, g, out)
+            want = expected_rs(orc, shapes, N, R, g, plan)
+            got = out.cpu().numpy()
+            assert same_f32(got, want), (j, R, first_mismatch(got, want))
+
+
+def test_concurrent_calls_on_one_plan(orc):
+    """Several host threads use one plan at once (each with its own stream
+    and output); results equal the oracle's."""
+    import threading
+    shapes = [(257, 9), (4096,), (3, 3)]
+    N = 4
+    plan = tide.Plan(shapes, N)
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=77))
+    outs = [fresh_out(plan.S) for _ in range(8)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for k in range(5):
+                    tide.rs(plan, t % N, g, outs[t], stream=s, small=(k % 2 == 1))
+            s.synchronize()
+        except Exception as exc:  # noqa: BLE001 - reported below
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for t in range(8):
+        want = expected_rs(orc, shapes, N, t % N, g, plan)
+        assert same_f32(outs[t].cpu().numpy(), want), t
