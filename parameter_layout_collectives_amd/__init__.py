@@ -11,6 +11,7 @@ TIDE-RS and TIDE-AG are described in "FSDPé€šä¿¡ç»ˆå±€ï¼šTIDEé›¶æ‹·è´é›†åˆé€šä
 (kongchang.com), Â§"TIDEçš„è®¾è®¡æ€è·¯ï¼šå¸ƒå±€æ„ŸçŸ¥çš„é›¶æ‹·è´é€šä¿¡".
 """
 import ctypes
+import sys
 
 import torch
 
@@ -62,15 +63,18 @@ class Plan:
         inner = (ctypes.c_int64 * max(P, 1))(*[_rows_inner(s)[1] for s in self.shapes])
         h = ctypes.c_void_p()
         self._h = None
+        self._destroy = lib().tide_plan_destroy
         _check(lib().tide_plan_create(self.world, P, d0, inner, int(align), ctypes.byref(h)))
         self._h = h
         self.S = int(lib().tide_plan_shard_numel(h))
         self.P = P
 
     def __del__(self):
-        if getattr(self, "_h", None) is not None:
-            lib().tide_plan_destroy(self._h)
-            self._h = None
+        # At interpreter exit the HIP runtime may already be torn down; the
+        # process is ending, so the plan's device tables go with it.
+        if getattr(self, "_h", None) is not None and not sys.is_finalizing():
+            self._destroy(self._h)
+        self._h = None
 
     @property
     def handle(self):

@@ -24,6 +24,9 @@ namespace tide {
 #ifndef TIDE_AG_TILE_SMALL
 #define TIDE_AG_TILE_SMALL 16384
 #endif
+#ifndef TIDE_RS_TILE_SMALL
+#define TIDE_RS_TILE_SMALL 2048
+#endif
 
 // Elements of one parameter segment handled by one reduce-scatter tile, and
 // by one all-gather tile.  Both are multiples of 8 so that tile starts keep
@@ -33,7 +36,9 @@ constexpr int64_t kAgTile = TIDE_AG_TILE;
 // Small-footprint all-gather launches keep one workgroup per CU resident, so
 // each one moves a larger tile to keep enough bytes in flight.
 constexpr int64_t kAgTileSmall = TIDE_AG_TILE_SMALL;
-static_assert(kRsTile % 8 == 0 && kAgTile % 8 == 0 && kAgTileSmall % 8 == 0,
+constexpr int64_t kRsTileSmall = TIDE_RS_TILE_SMALL;
+static_assert(kRsTile % 8 == 0 && kAgTile % 8 == 0 && kAgTileSmall % 8 == 0 &&
+                  kRsTileSmall % 8 == 0,
               "tiles must keep the 16-byte phase");
 static_assert(kAgTileSmall * 4 < (int64_t(1) << 31), "all-gather tile bytes must fit in int");
 constexpr int kBlock = 256;           // lanes per workgroup (4 wave64)
@@ -74,6 +79,7 @@ struct DeviceState {
     void *d_rs_tiles = nullptr;  // Tile[n_rs]
     void *d_ag_tiles = nullptr;  // Tile[n_ag]
     void *d_ag_tiles_small = nullptr;  // Tile[n_ag_small]
+    void *d_rs_tiles_small = nullptr;  // Tile[n_rs_small]
     std::vector<PtrTable> rs_cache, ag_cache;
     uint64_t tick = 0;
 };
@@ -87,7 +93,7 @@ struct tide_plan {
     int64_t align = 1, S = 0, psi = 0;
     std::vector<int64_t> d0, inner, c, seg, off, numel;
     std::vector<tide::ParamDesc> desc;
-    std::vector<tide::Tile> rs_tiles, ag_tiles, ag_tiles_small;
+    std::vector<tide::Tile> rs_tiles, rs_tiles_small, ag_tiles, ag_tiles_small;
     mutable std::mutex mu;
     mutable std::vector<tide::DeviceState *> devs;
 };

@@ -224,9 +224,12 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int64_t *dim0
         // Reduce-scatter tiles cover every position of a rank block: each
         // parameter's segment and the alignment gap after it (padding and
         // gaps are written as zeros).  They do not depend on the rank.
-        for (int32_t i = 0; i < nparams; i++)
+        for (int32_t i = 0; i < nparams; i++) {
             for (int64_t k = 0; k < p->desc[i].span; k += tide::kRsTile)
                 p->rs_tiles.push_back({i, 0, k});
+            for (int64_t k = 0; k < p->desc[i].span; k += tide::kRsTileSmall)
+                p->rs_tiles_small.push_back({i, 0, k});
+        }
         // All-gather tiles cover the real elements of every (param, rank);
         // ranks of one parameter are adjacent so the destination tensor is
         // written front to back.

@@ -159,7 +159,7 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t v, int64_t ntiles) {
 // TIDE-RS kernel
 // ---------------------------------------------------------------------------
 //
-// Tile t covers elements [k0, k0 + kRsTile) of parameter i's span in the
+// Tile t covers elements [k0, k0 + TILE) of parameter i's span in the
 // rank block (its segment plus any alignment gap after it).  For rank R:
 //   k <  L(R,i):  out[off_i + k] = sum_{r=0..N-1} widen(G[r][i][R*seg_i + k])
 //   k >= L(R,i):  out[off_i + k] = +0.0f   (padding rows, alignment gap)
@@ -172,7 +172,7 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t v, int64_t ntiles) {
 // 16-byte stores when its output offset is a multiple of 4 too.  With VEC = 4
 // every store instruction of a wave covers one contiguous 1 KiB span.
 // PACE > 0 makes each wave sleep between tiles (small-footprint launches).
-template <int BLOCK, int CPL, int VEC, int RB, int PACE, bool XMAP>
+template <int BLOCK, int CPL, int VEC, int RB, int PACE, bool XMAP, int64_t TILE>
 __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__ pdesc,
                                                    const Tile *__restrict__ tiles,
                                                    int64_t ntiles,
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
         int64_t L = d.numel - src;
         L = L < 0 ? 0 : (L > d.seg ? d.seg : L);
         const int64_t kb = tile.k0;
-        const int64_t ke = min(kb + kRsTile, d.span);
+        const int64_t ke = min(kb + TILE, d.span);
         const int64_t re = min(ke, L);
         float *__restrict__ o = out + d.off;
         const uint16_t *const *__restrict__ P = ptrs + static_cast<int64_t>(tile.param) * N;
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
             rs_elems<BLOCK>(P, N, src, o, kb, vs);
             rs_elems<BLOCK>(P, N, src, o, ve, re);
 
-            // A tile holds at most kRsTile/VEC chunks, so every per-lane
-            // byte offset below fits in 32 bits.
+            // A tile holds at most TILE/VEC chunks, so every per-lane byte
+            // offset below fits in 32 bits.
             const int nch = static_cast<int>((ve - vs) / VEC);
             const bool st16 = vec_out && (((d.off + vs) & 3) == 0);
             GLOBAL_AS char *obase = gstore_ptr<char>(o + vs);
@@ -368,13 +368,13 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
 #define TIDE_RS_RB 8
 #endif
 #ifndef TIDE_SMALL_CPL
-#define TIDE_SMALL_CPL 4
+#define TIDE_SMALL_CPL 2
 #endif
 #ifndef TIDE_SMALL_VEC
 #define TIDE_SMALL_VEC 4
 #endif
 #ifndef TIDE_SMALL_RB
-#define TIDE_SMALL_RB 8
+#define TIDE_SMALL_RB 16
 #endif
 #ifndef TIDE_SMALL_PERSISTENT
 #define TIDE_SMALL_PERSISTENT 0
@@ -429,6 +429,7 @@ void free_state(DeviceState *ds) {
     (void)hipFree(ds->d_rs_tiles);
     (void)hipFree(ds->d_ag_tiles);
     (void)hipFree(ds->d_ag_tiles_small);
+    (void)hipFree(ds->d_rs_tiles_small);
     for (auto &pt : ds->rs_cache) (void)hipFree(pt.dev);
     for (auto &pt : ds->ag_cache) (void)hipFree(pt.dev);
     delete ds;
@@ -473,6 +474,9 @@ tide_status device_state(const tide_plan *p, DeviceState **out) {
     if (st == TIDE_OK)
         st = upload(p->rs_tiles.data(), p->rs_tiles.size() * sizeof(Tile), &ds->d_rs_tiles,
                     "reduce-scatter tiles");
+    if (st == TIDE_OK)
+        st = upload(p->rs_tiles_small.data(), p->rs_tiles_small.size() * sizeof(Tile),
+                    &ds->d_rs_tiles_small, "reduce-scatter tiles (small footprint)");
     if (st == TIDE_OK)
         st = upload(p->ag_tiles.data(), p->ag_tiles.size() * sizeof(Tile), &ds->d_ag_tiles,
                     "all-gather tiles");
@@ -624,27 +628,31 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
     st = tide::pointer_table(ds, ds->rs_cache, key, dev_order, &pt);
     if (st != TIDE_OK) return st;
 
-    const int64_t ntiles = static_cast<int64_t>(plan->rs_tiles.size());
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    const int64_t ntiles =
+        static_cast<int64_t>(small ? plan->rs_tiles_small.size() : plan->rs_tiles.size());
     const unsigned grid = tide::grid_size(ds, ntiles, flags, max_workgroups);
     const int vec_in = pt->aligned16 ? 1 : 0;
     const int vec_out = (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0;
     (void)hipGetLastError();
     const auto *pd = static_cast<const tide::ParamDesc *>(ds->d_params);
-    const auto *tl = static_cast<const tide::Tile *>(ds->d_rs_tiles);
     const auto *gp = static_cast<const uint16_t *const *>(pt->dev);
-    if (flags & TIDE_F_SMALL_FOOTPRINT) {
+    if (small) {
         auto k = tide::rs_kernel<TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_VEC, TIDE_SMALL_RB,
-                                 TIDE_SMALL_PACE, TIDE_XMAP_RS>;
+                                 TIDE_SMALL_PACE, TIDE_XMAP_RS, tide::kRsTileSmall>;
         st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->small_lds);
         if (st != TIDE_OK) return st;
         hipLaunchKernelGGL(k, dim3(grid), dim3(TIDE_SMALL_BLOCK), ds->small_lds,
-                           static_cast<hipStream_t>(stream), pd, tl, ntiles, gp, plan->N, rank,
-                           out, vec_in, vec_out);
-    } else
+                           static_cast<hipStream_t>(stream), pd,
+                           static_cast<const tide::Tile *>(ds->d_rs_tiles_small), ntiles, gp,
+                           plan->N, rank, out, vec_in, vec_out);
+    } else {
         hipLaunchKernelGGL((tide::rs_kernel<tide::kBlock, tide::kRsChunksPerLane, TIDE_RS_VEC,
-                                            TIDE_RS_RB, 0, TIDE_XMAP_RS>),
-                           dim3(grid), dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream),
-                           pd, tl, ntiles, gp, plan->N, rank, out, vec_in, vec_out);
+                                            TIDE_RS_RB, 0, TIDE_XMAP_RS, tide::kRsTile>),
+                           dim3(grid), dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream), pd,
+                           static_cast<const tide::Tile *>(ds->d_rs_tiles), ntiles, gp, plan->N,
+                           rank, out, vec_in, vec_out);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
     tide::clear_error();
