@@ -75,6 +75,8 @@ struct DeviceState {
     int lds_per_cu = 0;          // bytes of LDS per compute unit
     int lds_per_wg_max = 0;      // largest LDS allocation one workgroup may make
     int small_lds = 0;           // LDS a small-footprint workgroup reserves (0 = none)
+    int rs_cap_lds = 0;          // LDS a default reduce-scatter workgroup reserves (0 = none)
+    int ag_cap_lds = 0;          // LDS a default all-gather workgroup reserves (0 = none)
     void *d_params = nullptr;    // ParamDesc[P]
     void *d_rs_tiles = nullptr;  // Tile[n_rs]
     void *d_ag_tiles = nullptr;  // Tile[n_ag]

@@ -115,11 +115,18 @@ __device__ __forceinline__ void rs_batch(const uint16_t *const *__restrict__ P, 
                                          int64_t first, const uint32_t *lane_off,
                                          f32x4 (*acc)[VEC / 4]) {
     typedef typename RsIn<VEC>::type V;
+    // All RB pointers of the batch in one go (one wide scalar load): the
+    // device pointer table carries kPtrPad spare entries after its end, so
+    // reading past the last rank of the last parameter stays in bounds.
+    // Pointers of ranks >= nb are never dereferenced.
+    const uint16_t *bp[RB];
+#pragma unroll
+    for (int q = 0; q < RB; q++) bp[q] = P[r0 + q];
     V v[RB][CPL];
 #pragma unroll
     for (int q = 0; q < RB; q++) {
         if (q < nb) {
-            const GLOBAL_AS char *base = gload_ptr<char>(P[r0 + q] + first);
+            const GLOBAL_AS char *base = gload_ptr<char>(bp[q] + first);
 #pragma unroll
             for (int j = 0; j < CPL; j++)
                 v[q][j] = stream_load(reinterpret_cast<const GLOBAL_AS V *>(base + lane_off[j]));
@@ -385,6 +392,12 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
 #ifndef TIDE_SMALL_AG_U
 #define TIDE_SMALL_AG_U 8
 #endif
+#ifndef TIDE_RS_WG_CAP
+#define TIDE_RS_WG_CAP 2
+#endif
+#ifndef TIDE_AG_WG_CAP
+#define TIDE_AG_WG_CAP 0
+#endif
 #ifndef TIDE_XMAP_AG
 #define TIDE_XMAP_AG 1
 #endif
@@ -398,6 +411,11 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
 #define TIDE_SMALL_WG 32
 #endif
 constexpr int kRsChunksPerLane = TIDE_RS_CPL;
+// Spare (null) entries after the reduce-scatter pointer table: a batch of RB
+// ranks loads its RB pointers unconditionally.
+constexpr size_t kPtrPad = 32;
+static_assert(TIDE_RS_RB <= static_cast<int>(kPtrPad) && TIDE_SMALL_RB <= static_cast<int>(kPtrPad),
+              "rank batch larger than the pointer-table padding");
 constexpr int kAgVecsPerLane = TIDE_AG_U;
 constexpr int kWgPerCu = TIDE_WG_PER_CU;      // default grid: enough waves to keep HBM busy
 constexpr int kSmallFootprintWg = TIDE_SMALL_WG;  // small-footprint grid
@@ -435,6 +453,13 @@ void free_state(DeviceState *ds) {
     delete ds;
 }
 
+// LDS that lets exactly `cap` workgroups share a CU (0: no cap).
+int lds_for_cap(const DeviceState *ds, int cap) {
+    if (cap <= 0 || ds->lds_per_cu <= 0) return 0;
+    const int want = ds->lds_per_cu / cap - 1024;
+    return (want > 0 && want <= ds->lds_per_wg_max) ? want : 0;
+}
+
 // The plan's tables on the current device (created on first use).
 // Caller holds p->mu.
 tide_status device_state(const tide_plan *p, DeviceState **out) {
@@ -469,6 +494,10 @@ tide_status device_state(const tide_plan *p, DeviceState **out) {
         const int want = ds->lds_per_cu / 2 + 1024;
         if (want <= ds->lds_per_wg_max) ds->small_lds = want;
     }
+    // Optional cap on default reduce-scatter workgroups per CU (same trick:
+    // an untouched LDS reservation of which exactly TIDE_RS_WG_CAP fit).
+    ds->rs_cap_lds = lds_for_cap(ds, TIDE_RS_WG_CAP);
+    ds->ag_cap_lds = lds_for_cap(ds, TIDE_AG_WG_CAP);
     tide_status st = upload(p->desc.data(), p->desc.size() * sizeof(ParamDesc), &ds->d_params,
                             "parameter table");
     if (st == TIDE_OK)
@@ -613,12 +642,14 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
         key.assign(reinterpret_cast<const uintptr_t *>(grads),
                    reinterpret_cast<const uintptr_t *>(grads) + n);
         dev_order.resize(n);
+        dev_order.reserve(n + tide::kPtrPad);
     } catch (const std::bad_alloc &) {
         return fail(TIDE_E_NOMEM, "tide_rs: out of host memory");
     }
     for (int32_t r = 0; r < plan->N; r++)
         for (int32_t i = 0; i < plan->P; i++)
             dev_order[static_cast<size_t>(i) * plan->N + r] = key[static_cast<size_t>(r) * plan->P + i];
+    dev_order.insert(dev_order.end(), tide::kPtrPad, 0);
 
     std::lock_guard<std::mutex> lock(plan->mu);
     tide::DeviceState *ds = nullptr;
@@ -647,9 +678,12 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
                            static_cast<const tide::Tile *>(ds->d_rs_tiles_small), ntiles, gp,
                            plan->N, rank, out, vec_in, vec_out);
     } else {
-        hipLaunchKernelGGL((tide::rs_kernel<tide::kBlock, tide::kRsChunksPerLane, TIDE_RS_VEC,
-                                            TIDE_RS_RB, 0, TIDE_XMAP_RS, tide::kRsTile>),
-                           dim3(grid), dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream), pd,
+        auto k = tide::rs_kernel<tide::kBlock, tide::kRsChunksPerLane, TIDE_RS_VEC, TIDE_RS_RB, 0,
+                                 TIDE_XMAP_RS, tide::kRsTile>;
+        st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->rs_cap_lds);
+        if (st != TIDE_OK) return st;
+        hipLaunchKernelGGL(k, dim3(grid), dim3(tide::kBlock), ds->rs_cap_lds,
+                           static_cast<hipStream_t>(stream), pd,
                            static_cast<const tide::Tile *>(ds->d_rs_tiles), ntiles, gp, plan->N,
                            rank, out, vec_in, vec_out);
     }
@@ -769,9 +803,11 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
                            static_cast<const tide::Tile *>(ds->d_ag_tiles_small), ntiles, pp,
                            plan->N, elem_bytes);
     } else {
-        hipLaunchKernelGGL((tide::ag_kernel<tide::kBlock, tide::kAgVecsPerLane, 0, TIDE_XMAP_AG,
-                                            tide::kAgTile>),
-                           dim3(grid), dim3(tide::kBlock), 0, static_cast<hipStream_t>(stream), pd,
+        auto k = tide::ag_kernel<tide::kBlock, tide::kAgVecsPerLane, 0, TIDE_XMAP_AG, tide::kAgTile>;
+        st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->ag_cap_lds);
+        if (st != TIDE_OK) return st;
+        hipLaunchKernelGGL(k, dim3(grid), dim3(tide::kBlock), ds->ag_cap_lds,
+                           static_cast<hipStream_t>(stream), pd,
                            static_cast<const tide::Tile *>(ds->d_ag_tiles), ntiles, pp, plan->N,
                            elem_bytes);
     }
