@@ -26,6 +26,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_LIB = os.path.join(HERE, "liboracle.so")
 
+# gradient element types of the reduce-scatter (codes of oracle.c)
+DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
+
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -88,12 +91,16 @@ class Oracle:
         lib.oracle_shard_run.argtypes = [_i32, _i64, _i64, _i32, _p, _p]
         lib.oracle_rs.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
         lib.oracle_rs_slices.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
+        lib.oracle_rs_typed.argtypes = [_i32, _i32, _p, _p, _i64, _i32, ctypes.c_int,
+                                        ctypes.c_int, _p, _p]
+        lib.oracle_rs_slices_typed.argtypes = [_i32, _i32, _p, _p, _i64, _i32, ctypes.c_int,
+                                               ctypes.c_int, _p, _p]
         lib.oracle_ag.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
         lib.oracle_rs_traffic.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         for fn in (lib.oracle_geometry, lib.oracle_shard_run, lib.oracle_rs,
-                   lib.oracle_rs_slices, lib.oracle_ag, lib.oracle_rs_traffic,
-                   lib.oracle_threads):
+                   lib.oracle_rs_slices, lib.oracle_rs_typed, lib.oracle_rs_slices_typed,
+                   lib.oracle_ag, lib.oracle_rs_traffic, lib.oracle_threads):
             fn.restype = ctypes.c_int
         lib.oracle_set_threads.restype = None
         self.lib = lib
@@ -134,42 +141,57 @@ class Oracle:
             raise ValueError("oracle_shard_run: invalid arguments")
         return int(src[0]), int(L[0])
 
-    def rs(self, shapes, N, R, grads, align=1):
-        """grads[r][i]: rank r's bf16 gradient of param i (uint16 bits, any
-        shape with d0*inner elements).  Returns rank R's fp32 block (S,)."""
+    @staticmethod
+    def _elems(a, dtype):
+        """Flat contiguous element array: uint16 bit patterns for bf16/f16,
+        float32 (or uint32 bit patterns, viewed as float32) for f32."""
+        if dtype == "f32":
+            a = np.ascontiguousarray(a)
+            if a.dtype != np.float32:
+                a = a.astype(np.uint32).view(np.float32) if a.dtype == np.uint32 else \
+                    np.ascontiguousarray(a, dtype=np.float32)
+            return a.reshape(-1)
+        return np.ascontiguousarray(a, dtype=np.uint16).reshape(-1)
+
+    def rs(self, shapes, N, R, grads, align=1, dtype="bf16", avg=False):
+        """grads[r][i]: rank r's gradient of param i (any shape with d0*inner
+        elements; uint16 bits for bf16/f16, float32 for f32).  Returns rank
+        R's fp32 block (S,): rank-order sum, or its mean if avg."""
         P = len(shapes)
         g = self.geometry(shapes, N, align)
         flat = []
         for r in range(N):
             for i in range(P):
-                a = np.ascontiguousarray(grads[r][i], dtype=np.uint16).reshape(-1)
+                a = self._elems(grads[r][i], dtype)
                 assert a.size == g.numel(i), (r, i, a.size, g.numel(i))
                 flat.append(a)
         d0, inner = self._dims(shapes)
         out = np.empty(g.S, np.float32)
-        rc = self.lib.oracle_rs(N, P, d0.ctypes.data, inner.ctypes.data, align, R,
-                                self._ptrs(flat), out.ctypes.data)
+        rc = self.lib.oracle_rs_typed(N, P, d0.ctypes.data, inner.ctypes.data, align, R,
+                                      DTYPES[dtype], int(bool(avg)), self._ptrs(flat),
+                                      out.ctypes.data)
         if rc != 0:
-            raise ValueError("oracle_rs: invalid arguments")
+            raise ValueError("oracle_rs_typed: invalid arguments")
         return out
 
-    def rs_slices(self, shapes, N, R, slices, align=1):
-        """slices[r][i]: the L(R,i) bf16 elements of rank r's gradient of
-        param i that fall in rank R's shard.  Returns rank R's block (S,)."""
+    def rs_slices(self, shapes, N, R, slices, align=1, dtype="bf16", avg=False):
+        """slices[r][i]: the L(R,i) elements of rank r's gradient of param i
+        that fall in rank R's shard.  Returns rank R's block (S,)."""
         P = len(shapes)
         g = self.geometry(shapes, N, align)
         flat = []
         for r in range(N):
             for i in range(P):
-                a = np.ascontiguousarray(slices[r][i], dtype=np.uint16).reshape(-1)
+                a = self._elems(slices[r][i], dtype)
                 assert a.size == g.run(R, i)[1], (r, i, a.size)
                 flat.append(a)
         d0, inner = self._dims(shapes)
         out = np.empty(g.S, np.float32)
-        rc = self.lib.oracle_rs_slices(N, P, d0.ctypes.data, inner.ctypes.data, align, R,
-                                       self._ptrs(flat), out.ctypes.data)
+        rc = self.lib.oracle_rs_slices_typed(N, P, d0.ctypes.data, inner.ctypes.data, align, R,
+                                             DTYPES[dtype], int(bool(avg)), self._ptrs(flat),
+                                             out.ctypes.data)
         if rc != 0:
-            raise ValueError("oracle_rs_slices: invalid arguments")
+            raise ValueError("oracle_rs_slices_typed: invalid arguments")
         return out
 
     def ag(self, shapes, N, rank_blocks, elem_bytes=2, align=1, fill=None):

@@ -22,7 +22,8 @@
  *          §"带宽饱和和节点扩展"    - a ring all-gather or reduce-scatter
  *            moves (N-1)/N * Psi elements per rank.
  *   [BLOG] tqpw.cn "FSDP技术演进全景图" §2.1 - each of N GPUs keeps 1/N of
- *            the parameters; §3.2 - reduction dtype float32.
+ *            the parameters; §3.2 - fp16 parameters with reduction dtype
+ *            float32 (hence fp16 gradients reduced in fp32).
  *
  * Readings taken where the pages are silent (each one listed in the design
  * notes of the repository):
@@ -36,7 +37,11 @@
  *     from rank 0's widened value (not from +0.0), round-to-nearest-even on
  *     every add, no fused operations, subnormals kept;
  *   - bf16 -> fp32 widening is exact: the fp32 bit pattern is the bf16
- *     pattern shifted left by 16.
+ *     pattern shifted left by 16; fp16 -> fp32 widening is exact too;
+ *   - the mean (when asked for) is the rank-order sum divided by N with one
+ *     correctly rounded binary32 division (the volume page describes the
+ *     reduce-scatter of gradients as averaging; the TIDE article as a
+ *     reduction to fp32; the sum is the default contract).
  *
  * Build: gcc -std=c11 -O2 -fno-fast-math -ffp-contract=off -fopenmp
  *        (see oracle/build_oracle.py).  OpenMP splits independent output
@@ -83,6 +88,46 @@ static float widen_bf16(uint16_t b)
     uint32_t bits = (uint32_t)b << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* IEEE binary16 -> binary32, exact (every half value is a float value).
+ * Fields: sign 1 bit, exponent 5 bits (bias 15), fraction 10 bits.
+ *   exponent 0:  zero or subnormal, value = fraction * 2^-24
+ *   exponent 31: infinity (fraction 0) or NaN (payload kept in the top
+ *                fraction bits of the float)
+ *   otherwise:   normal, float exponent = e - 15 + 127, fraction << 13 */
+static float widen_f16(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t e = (uint32_t)(h >> 10) & 0x1fu;
+    uint32_t frac = (uint32_t)h & 0x3ffu;
+    uint32_t bits;
+    float f;
+    if (e == 0) {
+        f = (float)frac * 0x1p-24f;     /* frac < 2^10: product exact */
+        return sign ? -f : f;
+    }
+    if (e == 31)
+        bits = (sign << 31) | 0x7f800000u | (frac << 13);
+    else
+        bits = (sign << 31) | ((e - 15u + 127u) << 23) | (frac << 13);
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* Gradient element types of the reduce-scatter. */
+#define ORACLE_BF16 0
+#define ORACLE_F16 1
+#define ORACLE_F32 2
+
+/* Element k of a gradient run, as an exact fp32 value. */
+static float load_elem(const void *run, int64_t k, int dtype)
+{
+    if (dtype == ORACLE_BF16) return widen_bf16(((const uint16_t *)run)[k]);
+    if (dtype == ORACLE_F16) return widen_f16(((const uint16_t *)run)[k]);
+    float f;
+    memcpy(&f, (const char *)run + 4 * k, sizeof f);
     return f;
 }
 
@@ -138,12 +183,16 @@ int oracle_shard_run(int32_t N, int64_t d0, int64_t inner, int32_t r,
 
 /* Shared body: `first[r*P + i]` points at element 0 of rank r's contribution
  * to rank R's shard of parameter i, i.e. at G[r][i] + src(R,i) for the
- * full-tensor entry point, or at the slice itself for the slice entry point. */
+ * full-tensor entry points, or at the slice itself for the slice entry
+ * points.  dtype is the gradient element type; avg != 0 divides each sum by
+ * N (one correctly rounded binary32 division), giving the mean. */
 static int rs_body(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner,
-                   int64_t align, int32_t R, const uint16_t *const *first, float *out)
+                   int64_t align, int32_t R, int dtype, int avg, const void *const *first,
+                   float *out)
 {
     int64_t S;
     if (N <= 0 || P <= 0 || R < 0 || R >= N) return ORACLE_EINVAL;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16 && dtype != ORACLE_F32) return ORACLE_EINVAL;
     int64_t *c = malloc(3 * sizeof(int64_t) * (size_t)P);
     if (!c) return ORACLE_EINVAL;
     int64_t *seg = c + P, *off = c + 2 * P;
@@ -167,9 +216,10 @@ static int rs_body(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner
             keep_subnormals();
 #pragma omp for schedule(static)
             for (int64_t k = 0; k < L; k++) {
-                float acc = widen_bf16(first[(int64_t)0 * P + i][k]);
+                float acc = load_elem(first[(int64_t)0 * P + i], k, dtype);
                 for (int32_t r = 1; r < N; r++)
-                    acc = acc + widen_bf16(first[(int64_t)r * P + i][k]);
+                    acc = acc + load_elem(first[(int64_t)r * P + i], k, dtype);
+                if (avg) acc = acc / (float)N;
                 out[off[i] + k] = acc;
             }
         }
@@ -179,31 +229,51 @@ static int rs_body(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner
     return ORACLE_OK;
 }
 
-/* grads[r*P + i] = rank r's full bf16 gradient of parameter i (d0*inner
- * elements, row-major).  out = S fp32 values, rank R's block. */
-int oracle_rs(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner,
-              int64_t align, int32_t R, const uint16_t *const *grads, float *out)
+static size_t elem_size(int dtype) { return dtype == ORACLE_F32 ? 4 : 2; }
+
+/* grads[r*P + i] = rank r's full gradient of parameter i (d0*inner
+ * elements of type dtype, row-major).  out = S fp32 values, rank R's block. */
+int oracle_rs_typed(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner,
+                    int64_t align, int32_t R, int dtype, int avg, const void *const *grads,
+                    float *out)
 {
     if (N <= 0 || P <= 0 || R < 0 || R >= N) return ORACLE_EINVAL;
-    const uint16_t **first = malloc(sizeof(uint16_t *) * (size_t)N * (size_t)P);
+    const void **first = malloc(sizeof(void *) * (size_t)N * (size_t)P);
     if (!first) return ORACLE_EINVAL;
     for (int32_t r = 0; r < N; r++)
         for (int32_t i = 0; i < P; i++) {
             int64_t src, L;
             shard_run(R, d0[i], inner[i], (d0[i] + N - 1) / N, &src, &L);
-            first[(int64_t)r * P + i] = L > 0 ? grads[(int64_t)r * P + i] + src : NULL;
+            first[(int64_t)r * P + i] =
+                L > 0 ? (const char *)grads[(int64_t)r * P + i] + (size_t)src * elem_size(dtype)
+                      : NULL;
         }
-    int rc = rs_body(N, P, d0, inner, align, R, first, out);
+    int rc = rs_body(N, P, d0, inner, align, R, dtype, avg, first, out);
     free(first);
     return rc;
 }
 
 /* slices[r*P + i] = the L(R,i) elements of rank r's gradient of parameter i
  * that belong to rank R's shard (G[r][i][src(R,i) .. src(R,i)+L(R,i)) ). */
+int oracle_rs_slices_typed(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner,
+                           int64_t align, int32_t R, int dtype, int avg,
+                           const void *const *slices, float *out)
+{
+    return rs_body(N, P, d0, inner, align, R, dtype, avg, slices, out);
+}
+
+/* The TIDE-RS contract: bf16 gradients, fp32 sum. */
+int oracle_rs(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner,
+              int64_t align, int32_t R, const uint16_t *const *grads, float *out)
+{
+    return oracle_rs_typed(N, P, d0, inner, align, R, ORACLE_BF16, 0,
+                           (const void *const *)grads, out);
+}
+
 int oracle_rs_slices(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner,
                      int64_t align, int32_t R, const uint16_t *const *slices, float *out)
 {
-    return rs_body(N, P, d0, inner, align, R, slices, out);
+    return rs_body(N, P, d0, inner, align, R, ORACLE_BF16, 0, (const void *const *)slices, out);
 }
 
 /* ---------------------------------------------------------------------- */

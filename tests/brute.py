@@ -159,3 +159,18 @@ def ag_by_concat(rank_blocks, shapes, N: int, align: int = 1):
         full = torch.cat(pieces) if pieces else torch.zeros(0)
         out.append(full.numpy())
     return out
+
+
+def round_f32(q: Fraction) -> np.float32:
+    """The binary32 value nearest to the rational q, ties to even (normal
+    range), found by exact comparison of the neighbours of a first guess."""
+    c = np.float32(float(q))
+    with np.errstate(all="ignore"):
+        cands = (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf)))
+    best = None
+    for cand in cands:
+        d = abs(Fraction(float(cand)) - q)
+        even = (int(np.array([cand], np.float32).view(np.uint32)[0]) & 1) == 0
+        if best is None or d < best[0] or (d == best[0] and even):
+            best = (d, cand)
+    return np.float32(best[1])

@@ -23,15 +23,15 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 MUTANTS = {
     "drop_last_rank": ("for (int32_t r = 1; r < N; r++)\n                    acc",
                        "for (int32_t r = 1; r < N - 1; r++)\n                    acc"),
-    "sum_from_plus_zero": ("float acc = widen_bf16(first[(int64_t)0 * P + i][k]);\n"
+    "sum_from_plus_zero": ("float acc = load_elem(first[(int64_t)0 * P + i], k, dtype);\n"
                            "                for (int32_t r = 1;",
                            "float acc = 0.0f;\n                for (int32_t r = 0;"),
-    "reverse_rank_order": ("float acc = widen_bf16(first[(int64_t)0 * P + i][k]);\n"
+    "reverse_rank_order": ("float acc = load_elem(first[(int64_t)0 * P + i], k, dtype);\n"
                            "                for (int32_t r = 1; r < N; r++)\n"
-                           "                    acc = acc + widen_bf16(first[(int64_t)r * P + i][k]);",
-                           "float acc = widen_bf16(first[(int64_t)(N - 1) * P + i][k]);\n"
+                           "                    acc = acc + load_elem(first[(int64_t)r * P + i], k, dtype);",
+                           "float acc = load_elem(first[(int64_t)(N - 1) * P + i], k, dtype);\n"
                            "                for (int32_t r = 1; r < N; r++)\n"
-                           "                    acc = acc + widen_bf16(first[(int64_t)(N - 1 - r) * P + i][k]);"),
+                           "                    acc = acc + load_elem(first[(int64_t)(N - 1 - r) * P + i], k, dtype);"),
     "floor_rows": ("c[i] = (d0[i] + N - 1) / N;", "c[i] = d0[i] / N + (d0[i] % N > 1);"),
     "ignore_align": ("off[i] = round_up(pos, align);", "off[i] = pos;"),
     "src_without_inner": ("*src = (int64_t)r * c * inner;", "*src = (int64_t)r * c;"),
@@ -47,6 +47,18 @@ MUTANTS = {
     "shard_owner_off_by_one": ("int64_t rows = d0 - (int64_t)r * c;",
                                "int64_t rows = d0 - (int64_t)(r + (r > 1)) * c;"),
     "skip_last_tail_round": ("*S = round_up(pos, align);", "*S = pos;"),
+    "mean_not_divided": ("if (avg) acc = acc / (float)N;", "(void)avg;"),
+    "mean_divides_by_n_minus_1": ("if (avg) acc = acc / (float)N;",
+                                  "if (avg) acc = acc / (float)(N > 1 ? N - 1 : 1);"),
+    "mean_by_reciprocal": ("if (avg) acc = acc / (float)N;",
+                           "if (avg) acc = acc * (1.0f / (float)N);"),
+    "f16_wrong_bias": ("bits = (sign << 31) | ((e - 15u + 127u) << 23) | (frac << 13);",
+                       "bits = (sign << 31) | ((e - 16u + 127u) << 23) | (frac << 13);"),
+    "f16_subnormal_scale": ("f = (float)frac * 0x1p-24f;", "f = (float)frac * 0x1p-25f;"),
+    "f16_nan_drops_payload": ("bits = (sign << 31) | 0x7f800000u | (frac << 13);",
+                              "bits = (sign << 31) | 0x7f800000u | (frac ? 0x400000u : 0u);"),
+    "f32_read_as_half_width": ("memcpy(&f, (const char *)run + 4 * k, sizeof f);",
+                               "memcpy(&f, (const char *)run + 2 * k, sizeof f);"),
 }
 
 

@@ -17,10 +17,15 @@ Pins used (none of them re-types the oracle's formulas):
     sum), rank order fixed by a cancellation case, -0.0, subnormals, Inf/NaN;
   * the recursive-summation error bound against an exact rational sum;
   * all-gather invariants: AG of the shards is the identity, and RS for
-    every rank followed by AG is the per-element rank-order all-reduce.
+    every rank followed by AG is the per-element rank-order all-reduce;
+  * gradient element types and the mean: every binary16 pattern widened as
+    numpy does, N=2 and integer-valued sums of fp16/fp32 gradients, the mean
+    as an exact power-of-two scaling (N = 2^k) or as the exact rational
+    sum/N rounded to nearest even (other N).
 """
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -301,6 +306,93 @@ def pin_rs_slices_match_full(orc):
         a = orc.rs(shapes, 4, R, grads)
         b = orc.rs_slices(shapes, 4, R, slices)
         assert np.array_equal(bits_f32(a), bits_f32(b))
+
+
+# --------------------------------------------------------------------------
+# gradient element types and the mean
+# --------------------------------------------------------------------------
+def _rand_typed(shapes, N, seed, dtype):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(N):
+        row = []
+        for s in shapes:
+            x = rng.standard_normal(s).astype(np.float32)
+            row.append(x.astype(np.float16).view(np.uint16) if dtype == "f16" else x)
+        out.append(row)
+    return out
+
+
+def pin_f16_widening_exhaustive(orc):
+    # every binary16 pattern against numpy's float16 -> float32 conversion
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    out = orc.rs([(65536,)], 1, 0, [[bits]], dtype="f16")
+    want = bits.view(np.float16).astype(np.float32)
+    assert np.array_equal(bits_f32(out), bits_f32(want))
+
+
+def pin_typed_n2_is_library_sum(orc):
+    shapes = [(9, 5), (4,)]
+    for dtype in ("f16", "f32"):
+        grads = _rand_typed(shapes, 2, 8, dtype)
+        g = orc.geometry(shapes, 2)
+        for R in range(2):
+            out = orc.rs(shapes, 2, R, grads, dtype=dtype)
+            for i in range(len(shapes)):
+                src, L = g.run(R, i)
+                ts = [torch.from_numpy(grads[r][i].reshape(-1)[src:src + L].copy())
+                      for r in range(2)]
+                if dtype == "f16":
+                    ts = [t.view(torch.float16) for t in ts]
+                want = torch.stack(ts).float().sum(0).numpy()
+                assert np.array_equal(bits_f32(out[g.off[i]:g.off[i] + L]), bits_f32(want)), \
+                    (dtype, R, i)
+
+
+def pin_typed_integer_exact(orc):
+    rng = np.random.default_rng(17)
+    shapes = [(11, 3), (7,)]
+    for dtype in ("f16", "f32"):
+        for N in (3, 16):
+            ints = [[rng.integers(-64, 65, size=s) for s in shapes] for _ in range(N)]
+            grads = [[a.astype(np.float16).view(np.uint16) if dtype == "f16" else
+                      a.astype(np.float32) for a in row] for row in ints]
+            g = orc.geometry(shapes, N)
+            for R in range(N):
+                out = orc.rs(shapes, N, R, grads, dtype=dtype)
+                for i in range(len(shapes)):
+                    src, L = g.run(R, i)
+                    want = sum(ints[r][i].reshape(-1)[src:src + L].astype(np.int64)
+                               for r in range(N))
+                    got = out[g.off[i]:g.off[i] + L]
+                    assert np.array_equal(got.astype(np.int64), want), (dtype, N, R, i)
+
+
+def pin_mean_power_of_two(orc):
+    # N = 2^k: the mean is the sum scaled by 2^-k, which is exact here
+    shapes = [(40, 3), (9,)]
+    for N, k in ((2, 1), (4, 2), (8, 3), (16, 4)):
+        grads = _rand_case(shapes, N, 30 + N)
+        for R in (0, N - 1):
+            s_ = orc.rs(shapes, N, R, grads)
+            m = orc.rs(shapes, N, R, grads, avg=True)
+            assert np.array_equal(bits_f32(m), bits_f32(np.ldexp(s_, -k).astype(np.float32)))
+
+
+def pin_mean_exact_rounding(orc):
+    # other N: the mean is the exact rational sum/N rounded to nearest even
+    shapes = [(17, 3)]
+    for N in (3, 5, 7, 13):
+        grads = _rand_case(shapes, N, 50 + N)
+        for R in (0, N - 1):
+            s_ = orc.rs(shapes, N, R, grads)
+            m = orc.rs(shapes, N, R, grads, avg=True)
+            g = orc.geometry(shapes, N)
+            src, L = g.run(R, 0)
+            for k in range(L):
+                want = brute.round_f32(Fraction(float(s_[k])) / N)
+                assert bits_f32([m[k]])[0] == bits_f32([want])[0], (N, R, k)
+            assert np.all(bits_f32(m[L:g.seg[0]]) == 0)          # padding stays +0
 
 
 # --------------------------------------------------------------------------
