@@ -341,7 +341,7 @@ def corun_ag(step, gemm):
 # CPU baseline: the oracle on the same step
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(step, reps=3):
+def cpu_baseline(step, min_reps=3, max_reps=40, budget_s=10.0):
     import numpy as np
 
     import oracle
@@ -360,7 +360,10 @@ def cpu_baseline(step, reps=3):
     host = step.gathered.view(torch.int16).cpu().numpy().view(np.uint16)
     blocks = [host[r * S:(r + 1) * S] for r in range(N)]
     t_rs, t_ag = [], []
-    for k in range(reps):
+    start = time.perf_counter()
+    for k in range(max_reps):
+        if k >= min_reps and time.perf_counter() - start > budget_s:
+            break
         t0 = time.perf_counter()
         orc.rs_slices(w.shapes, N, R, slices)
         t1 = time.perf_counter()
@@ -368,7 +371,8 @@ def cpu_baseline(step, reps=3):
         t2 = time.perf_counter()
         t_rs.append(t1 - t0)
         t_ag.append(t2 - t1)
-        log(f"cpu baseline rep {k}: rs {t1 - t0:.3f} s, ag {t2 - t1:.3f} s")
+        if k < 3:
+            log(f"cpu baseline rep {k}: rs {t1 - t0:.3f} s, ag {t2 - t1:.3f} s")
     trs, tag = statistics.median(t_rs), statistics.median(t_ag)
     cpu = "unknown"
     try:
@@ -385,7 +389,7 @@ def cpu_baseline(step, reps=3):
         "kind": "oracle",
         "sample": (f"one full step of {w.name} (tide_rs for rank 0 from host copies of its "
                    f"{N}x{plan.P} gradient slices + tide_ag of the {N}x{S} gathered buffer), "
-                   f"median of {reps}; host copies not timed"),
+                   f"median of {len(t_rs)} repetitions (~{budget_s:.0f} s); host copies not timed"),
         "rs_s": trs,
         "ag_s": tag,
         "cpu_model": cpu,

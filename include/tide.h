@@ -88,6 +88,20 @@ typedef struct tide_plan tide_plan;
  * tide_rs rejects it with TIDE_E_UNSUPPORTED: a reduction needs arithmetic. */
 #define TIDE_F_COPY_ENGINE 0x2u
 
+/* Flags, tide_rs only: the gradient element type.  Without either flag the
+ * gradients are bf16 (the TIDE-RS case).  TIDE_F_GRAD_F16 reads IEEE fp16
+ * gradients (FSDP mixed precision with fp16 parameters and an fp32 reduce,
+ * tqpw.cn blog §3.2); TIDE_F_GRAD_F32 reads fp32 gradients.  Both widen
+ * exactly to fp32 before the rank-order sum.  Setting both is rejected. */
+#define TIDE_F_GRAD_F16 0x8u
+#define TIDE_F_GRAD_F32 0x10u
+
+/* Flag, tide_rs only: write the mean instead of the sum - each rank-order
+ * fp32 sum divided by N with one correctly rounded binary32 division
+ * (apxml "Communication volume analysis" §"分片中的通信原语" describes the
+ * gradient reduce-scatter as averaging).  Padding and gaps stay +0.0f. */
+#define TIDE_F_AVG 0x4u
+
 /* ---------------------------------------------------------------------- */
 /* Plan (host only; makes no HIP call).                                    */
 /* ---------------------------------------------------------------------- */
@@ -129,19 +143,23 @@ tide_status tide_plan_real(const tide_plan *plan, int32_t rank, int32_t i,
 /* Write rank `rank`'s fp32 block (S floats) of the reduce-scatter:
  *   out[off_i + k] = sum over r = 0..N-1, in that order, of
  *                    widen(grads[r*P + i][src(rank,i) + k])   for k < L(rank,i)
+ *                    (divided by N with TIDE_F_AVG)
  *   out[off_i + k] = +0.0f for L(rank,i) <= k < seg_i, and gaps are +0.0f.
- * widen(b) is exact (bf16 bits shifted into the top of an fp32); every add
- * is one IEEE binary32 round-to-nearest-even addition with subnormals kept,
- * so the result is bit-for-bit reproducible.
+ * widen(b) is exact (bf16 bits shifted into the top of an fp32; fp16 and
+ * fp32 convert exactly); every add is one IEEE binary32 round-to-nearest-even
+ * addition with subnormals kept, so the result is bit-for-bit reproducible.
  *   plan    a plan from tide_plan_create.
  *   rank    0 <= rank < N.
- *   grads   host array of N*P device pointers; entry r*P + i is rank r's bf16
+ *   grads   host array of N*P device pointers; entry r*P + i is rank r's
  *           gradient of parameter i, dim0_i*inner_i elements, row-major,
- *           2-byte aligned.  Only the elements of rank `rank`'s shard are
- *           read.  Entries with L(rank,i) = 0 may be NULL.
+ *           aligned to its element size (bf16 by default, fp16 or fp32 by
+ *           flag).  Only the elements of rank `rank`'s shard are read.
+ *           Entries with L(rank,i) = 0 may be NULL.
  *   out     device pointer to S floats (4-byte aligned), e.g. block `rank`
  *           of an N*S buffer; must not overlap any element that is read.
- *   flags   0 or TIDE_F_SMALL_FOOTPRINT; other bits -> TIDE_E_UNSUPPORTED.
+ *   flags   any of TIDE_F_SMALL_FOOTPRINT, TIDE_F_AVG and one of
+ *           TIDE_F_GRAD_F16 / TIDE_F_GRAD_F32 (both: TIDE_E_INVALID);
+ *           TIDE_F_COPY_ENGINE or other bits -> TIDE_E_UNSUPPORTED.
  *   max_workgroups  0 = the policy for `flags`; > 0 caps the grid.
  *   stream  hipStream_t (NULL = null stream).
  * 16-byte aligned pointers take the vector path; other alignments are

@@ -19,6 +19,12 @@ from ._lib import lib
 
 SMALL_FOOTPRINT = 0x1
 COPY_ENGINE = 0x2
+AVG = 0x4
+GRAD_F16 = 0x8
+GRAD_F32 = 0x10
+
+# gradient dtype -> tide_rs flag selecting it
+_GRAD_FLAG = {torch.bfloat16: 0, torch.float16: GRAD_F16, torch.float32: GRAD_F32}
 
 _STATUS = {0: "TIDE_OK", 1: "TIDE_E_INVALID", 2: "TIDE_E_UNSUPPORTED", 3: "TIDE_E_NOMEM",
            4: "TIDE_E_HIP"}
@@ -69,10 +75,11 @@ class Plan:
         self.S = int(lib().tide_plan_shard_numel(h))
         self.P = P
 
-    def __del__(self):
-        # At interpreter exit the HIP runtime may already be torn down; the
-        # process is ending, so the plan's device tables go with it.
-        if getattr(self, "_h", None) is not None and not sys.is_finalizing():
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # At interpreter exit the HIP runtime may already be torn down (and
+        # module globals cleared); the process is ending, so the plan's device
+        # tables go with it.
+        if getattr(self, "_h", None) is not None and not _finalizing():
             self._destroy(self._h)
         self._h = None
 
@@ -98,30 +105,40 @@ class PointerTable:
     """A host array of device pointers kept alive with the tensors it names.
     Build it once and pass it to rs/ag repeatedly to skip re-marshalling."""
 
-    def __init__(self, tensors):
+    def __init__(self, tensors, dtype=None):
         self.tensors = list(tensors)
+        self.dtype = dtype
         self.array = (ctypes.c_void_p * max(len(self.tensors), 1))(
             *[t.data_ptr() if t is not None else None for t in self.tensors])
 
 
 def grad_table(plan, grads):
-    """PointerTable for tide_rs: grads[r][i] = rank r's bf16 gradient of param i."""
+    """PointerTable for tide_rs: grads[r][i] = rank r's gradient of param i,
+    all bf16, all fp16 or all fp32."""
     if len(grads) != plan.world:
         raise ValueError(f"expected {plan.world} ranks of gradients, got {len(grads)}")
-    flat = []
+    dtype = None
     for r, rank in enumerate(grads):
         if len(rank) != plan.P:
             raise ValueError(f"rank {r}: expected {plan.P} gradients, got {len(rank)}")
         for i, t in enumerate(rank):
-            if t.dtype != torch.bfloat16:
-                raise TypeError(f"grads[{r}][{i}] must be bfloat16, got {t.dtype}")
+            if t.dtype not in _GRAD_FLAG:
+                raise TypeError(f"grads[{r}][{i}] must be bfloat16, float16 or float32, "
+                                f"got {t.dtype}")
+            if dtype is None:
+                dtype = t.dtype
+            elif t.dtype != dtype:
+                raise TypeError(f"grads[{r}][{i}] is {t.dtype}, the others are {dtype}")
+    flat = []
+    for r, rank in enumerate(grads):
+        for i, t in enumerate(rank):
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"grads[{r}][{i}] must be a contiguous device tensor")
             if t.numel() != _numel(plan.shapes[i]):
                 raise ValueError(f"grads[{r}][{i}] has {t.numel()} elements, "
                                  f"expected {_numel(plan.shapes[i])}")
             flat.append(t)
-    return PointerTable(flat)
+    return PointerTable(flat, dtype)
 
 
 def _numel(shape):
@@ -131,21 +148,23 @@ def _numel(shape):
     return n
 
 
-def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None):
+def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=False):
     """TIDE-RS: write rank `rank`'s fp32 block (plan.S floats) into `out`.
 
-    grads: list over ranks of lists over params of bf16 device tensors, or a
-    PointerTable from grad_table().  out: contiguous fp32 device tensor with
-    plan.S elements (e.g. a row of an [N, S] buffer)."""
+    grads: list over ranks of lists over params of device tensors (bf16,
+    fp16 or fp32, one dtype for all), or a PointerTable from grad_table().
+    out: contiguous fp32 device tensor with plan.S elements (e.g. a row of an
+    [N, S] buffer).  avg: write the mean (sum / N) instead of the sum."""
     if not isinstance(grads, PointerTable):
         grads = grad_table(plan, grads)
     if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 device tensor")
     if out.numel() != plan.S:
         raise ValueError(f"out has {out.numel()} elements, expected S = {plan.S}")
+    flags = _GRAD_FLAG.get(grads.dtype, 0)
+    flags |= (SMALL_FOOTPRINT if small else 0) | (AVG if avg else 0)
     _check(lib().tide_rs(plan.handle, int(rank), grads.array, ctypes.c_void_p(out.data_ptr()),
-                         SMALL_FOOTPRINT if small else 0, int(max_workgroups),
-                         _stream_handle(stream)))
+                         flags, int(max_workgroups), _stream_handle(stream)))
 
 
 _ELEM = {torch.bfloat16: 2, torch.float16: 2, torch.int16: 2, torch.float32: 4, torch.int32: 4}
@@ -195,6 +214,7 @@ def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, table
                          _stream_handle(stream)))
 
 
-__all__ = ["Plan", "PointerTable", "TideError", "SMALL_FOOTPRINT", "COPY_ENGINE", "grad_table",
+__all__ = ["Plan", "PointerTable", "TideError", "SMALL_FOOTPRINT", "COPY_ENGINE", "AVG",
+           "GRAD_F16", "GRAD_F32", "grad_table",
            "ag_tables",
            "rs", "ag", "lib"]

@@ -71,8 +71,11 @@ tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *g
     if (flags & TIDE_F_COPY_ENGINE)
         return fail(TIDE_E_UNSUPPORTED,
                     "tide_rs: TIDE_F_COPY_ENGINE is for tide_ag (a reduction needs arithmetic)");
-    if (flags & ~TIDE_F_SMALL_FOOTPRINT)
+    if (flags & ~(TIDE_F_SMALL_FOOTPRINT | TIDE_F_AVG | TIDE_F_GRAD_F16 | TIDE_F_GRAD_F32))
         return fail(TIDE_E_UNSUPPORTED, "tide_rs: unknown flag bits");
+    if ((flags & TIDE_F_GRAD_F16) && (flags & TIDE_F_GRAD_F32))
+        return fail(TIDE_E_INVALID, "tide_rs: TIDE_F_GRAD_F16 and TIDE_F_GRAD_F32 both set");
+    const uintptr_t es = (flags & TIDE_F_GRAD_F32) ? 4u : 2u;
     if (max_wg < 0) return fail(TIDE_E_INVALID, "tide_rs: max_workgroups < 0");
     if (p->S == 0) return TIDE_OK;
     if (!grads) return fail(TIDE_E_INVALID, "tide_rs: grads array is NULL");
@@ -93,11 +96,12 @@ tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *g
                 return fail(TIDE_E_INVALID, "tide_rs: grads[" + std::to_string(r) + "*P+" +
                                                 std::to_string(i) + "] is NULL");
             const uintptr_t a = reinterpret_cast<uintptr_t>(g);
-            if (a & 1)
+            if (a % es)
                 return fail(TIDE_E_INVALID, "tide_rs: grads[" + std::to_string(r) + "*P+" +
-                                                std::to_string(i) + "] is not 2-byte aligned");
-            spans.push_back({a + static_cast<uintptr_t>(src) * 2u,
-                             a + static_cast<uintptr_t>(src + L) * 2u, false});
+                                                std::to_string(i) +
+                                                "] is not aligned to its element size");
+            spans.push_back({a + static_cast<uintptr_t>(src) * es,
+                             a + static_cast<uintptr_t>(src + L) * es, false});
         }
     }
     if (written_overlaps(spans))

@@ -73,60 +73,94 @@ __device__ __forceinline__ void stream_store(V v, GLOBAL_AS V *p) {
 #endif
 }
 
-// bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one.
+// Gradient element types.  Each widens exactly to fp32: bf16 is the top
+// half of an fp32 pattern, every fp16 value is an fp32 value, fp32 is kept.
+enum GradType { kBf16 = 0, kF16 = 1, kF32 = 2 };
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float bf16_at(const uint16_t *p) {
-    return __uint_as_float(static_cast<uint32_t>(*gload_ptr<uint16_t>(p)) << 16);
+__device__ __forceinline__ float f16_to_f32(uint32_t h16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h16)));
 }
 
-// Four fp32 values from two words holding four consecutive bf16 (the element
-// with the lower address sits in the low half of its word).
-__device__ __forceinline__ f32x4 widen4(uint32_t w0, uint32_t w1) {
-    return f32x4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
-}
+// Per type: element bytes, the vector holding 4 consecutive elements, and
+// the exact widening of such a vector and of one element.  (In a word of
+// two 16-bit elements the lower address sits in the low half.)
+template <int IT> struct Grad;
+template <> struct Grad<kBf16> {
+    static constexpr int ES = 2;
+    typedef u32x2 V4;
+    static __device__ __forceinline__ f32x4 widen(V4 v) {
+        return f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+    }
+    static __device__ __forceinline__ float one(const GLOBAL_AS char *p) {
+        return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const GLOBAL_AS uint16_t *>(p))
+                               << 16);
+    }
+};
+template <> struct Grad<kF16> {
+    static constexpr int ES = 2;
+    typedef u32x2 V4;
+    static __device__ __forceinline__ f32x4 widen(V4 v) {
+        return f32x4{f16_to_f32(v.x & 0xffffu), f16_to_f32(v.x >> 16), f16_to_f32(v.y & 0xffffu),
+                     f16_to_f32(v.y >> 16)};
+    }
+    static __device__ __forceinline__ float one(const GLOBAL_AS char *p) {
+        return f16_to_f32(*reinterpret_cast<const GLOBAL_AS uint16_t *>(p));
+    }
+};
+template <> struct Grad<kF32> {
+    static constexpr int ES = 4;
+    typedef u32x4 V4;
+    static __device__ __forceinline__ f32x4 widen(V4 v) {
+        return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w)};
+    }
+    static __device__ __forceinline__ float one(const GLOBAL_AS char *p) {
+        return *reinterpret_cast<const GLOBAL_AS float *>(p);
+    }
+};
 
 // Scalar path for elements [a, b) of a segment: one lane per element, the
-// same rank-order sum as the vector path.
-template <int BLOCK>
-__device__ __forceinline__ void rs_elems(const uint16_t *const *__restrict__ P, int N,
+// same rank-order sum (and mean) as the vector path.  P[r] is rank r's
+// gradient; src is rank R's first element in it.
+template <int IT, int BLOCK>
+__device__ __forceinline__ void rs_elems(const char *const *__restrict__ P, int N, int avg,
                                          int64_t src, float *__restrict__ o, int64_t a,
                                          int64_t b) {
+    typedef Grad<IT> G;
     for (int64_t k = a + threadIdx.x; k < b; k += BLOCK) {
-        float acc = bf16_at(P[0] + src + k);
-        for (int r = 1; r < N; r++) acc = acc + bf16_at(P[r] + src + k);
+        const int64_t byte = (src + k) * G::ES;
+        float acc = G::one(gload_ptr<char>(P[0] + byte));
+        for (int r = 1; r < N; r++) acc = acc + G::one(gload_ptr<char>(P[r] + byte));
+        if (avg) acc = acc / static_cast<float>(N);
         o[k] = acc;
     }
 }
 
-// VEC consecutive bf16 per lane and chunk: 16-byte loads for VEC = 8,
-// 8-byte loads for VEC = 4.
-template <int VEC> struct RsIn;
-template <> struct RsIn<8> { typedef u32x4 type; };
-template <> struct RsIn<4> { typedef u32x2 type; };
-
-// Loads one batch of up to RB ranks, all issued before any add, then adds
-// them in rank order.  FIRST: the batch starts at rank 0, whose value
-// initialises the sums.  `first` = src + (first element of this tile's
-// vector range), wave-uniform; lane_off[j] is each lane's chunk start
-// relative to it, in bytes (fits in 32 bits).
-template <int CPL, int VEC, int RB, bool FIRST>
-__device__ __forceinline__ void rs_batch(const uint16_t *const *__restrict__ P, int r0, int nb,
-                                         int64_t first, const uint32_t *lane_off,
-                                         f32x4 (*acc)[VEC / 4]) {
-    typedef typename RsIn<VEC>::type V;
+// Loads one batch of up to RB ranks (4 elements per lane and chunk), all
+// issued before any add, then adds them in rank order.  FIRST: the batch
+// starts at rank 0, whose value initialises the sums.  `first_byte` is the
+// wave-uniform byte offset of this tile's vector range in each gradient;
+// lane_off[j] is each lane's chunk start relative to it, in bytes.
+template <int IT, int CPL, int RB, bool FIRST>
+__device__ __forceinline__ void rs_batch(const char *const *__restrict__ P, int r0, int nb,
+                                         int64_t first_byte, const uint32_t *lane_off,
+                                         f32x4 *acc) {
+    typedef Grad<IT> G;
+    typedef typename G::V4 V;
     // All RB pointers of the batch in one go (one wide scalar load): the
     // device pointer table carries kPtrPad spare entries after its end, so
     // reading past the last rank of the last parameter stays in bounds.
     // Pointers of ranks >= nb are never dereferenced.
-    const uint16_t *bp[RB];
+    const char *bp[RB];
 #pragma unroll
     for (int q = 0; q < RB; q++) bp[q] = P[r0 + q];
     V v[RB][CPL];
 #pragma unroll
     for (int q = 0; q < RB; q++) {
         if (q < nb) {
-            const GLOBAL_AS char *base = gload_ptr<char>(bp[q] + first);
+            const GLOBAL_AS char *base = gload_ptr<char>(bp[q] + first_byte);
 #pragma unroll
             for (int j = 0; j < CPL; j++)
                 v[q][j] = stream_load(reinterpret_cast<const GLOBAL_AS V *>(base + lane_off[j]));
@@ -137,14 +171,11 @@ __device__ __forceinline__ void rs_batch(const uint16_t *const *__restrict__ P, 
         if (q < nb) {
 #pragma unroll
             for (int j = 0; j < CPL; j++) {
-#pragma unroll
-                for (int h = 0; h < VEC / 4; h++) {
-                    const f32x4 x = widen4(v[q][j][2 * h], v[q][j][2 * h + 1]);
-                    if (FIRST && q == 0)
-                        acc[j][h] = x;
-                    else
-                        acc[j][h] = acc[j][h] + x;
-                }
+                const f32x4 x = G::widen(v[q][j]);
+                if (FIRST && q == 0)
+                    acc[j] = x;
+                else
+                    acc[j] = acc[j] + x;
             }
         }
     }
@@ -166,26 +197,29 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t v, int64_t ntiles) {
 // TIDE-RS kernel
 // ---------------------------------------------------------------------------
 //
-// Tile t covers elements [k0, k0 + TILE) of parameter i's span in the
-// rank block (its segment plus any alignment gap after it).  For rank R:
+// Tile t covers elements [k0, k0 + TILE) of parameter i's span in the rank
+// block (its segment plus any alignment gap after it).  For rank R:
 //   k <  L(R,i):  out[off_i + k] = sum_{r=0..N-1} widen(G[r][i][R*seg_i + k])
+//                 (divided by N when avg is set)
 //   k >= L(R,i):  out[off_i + k] = +0.0f   (padding rows, alignment gap)
 // ptrs is param-major: ptrs[i*N + r] = G[r][i].
 //
-// vec_in: every gradient pointer is 16-byte aligned, so lanes take chunks of
-// VEC elements whose source address is VEC*2-byte aligned; the few elements
-// before the first and after the last chunk of a tile take the scalar path.
-// vec_out: `out` is 16-byte aligned; a chunk's VEC fp32 results go out as
-// 16-byte stores when its output offset is a multiple of 4 too.  With VEC = 4
-// every store instruction of a wave covers one contiguous 1 KiB span.
-// PACE > 0 makes each wave sleep between tiles (small-footprint launches).
-template <int BLOCK, int CPL, int VEC, int RB, int PACE, bool XMAP, int64_t TILE>
+// Lanes take chunks of 4 consecutive elements: 8-byte loads for 16-bit
+// gradients, 16-byte loads for fp32 ones.  vec_in: every gradient pointer is
+// 16-byte aligned, so chunks start where src + k is a multiple of 4; the few
+// elements before the first and after the last chunk of a tile take the
+// scalar path.  vec_out: `out` is 16-byte aligned; a chunk's 4 fp32 results
+// go out as one 16-byte store when its output offset is a multiple of 4 too,
+// so every store instruction of a wave covers one contiguous 1 KiB span.
+// PACE > 0 makes each wave sleep between tiles.
+template <int IT, int BLOCK, int CPL, int RB, int PACE, bool XMAP, int64_t TILE>
 __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__ pdesc,
                                                    const Tile *__restrict__ tiles,
                                                    int64_t ntiles,
-                                                   const uint16_t *const *__restrict__ ptrs,
-                                                   int N, int R, float *__restrict__ out,
+                                                   const char *const *__restrict__ ptrs,
+                                                   int N, int R, int avg, float *__restrict__ out,
                                                    int vec_in, int vec_out) {
+    constexpr int ES = Grad<IT>::ES;
     for (int64_t v = blockIdx.x; v < ntiles; v += gridDim.x) {
         const Tile tile = tiles[XMAP ? xcd_tile(v, ntiles) : v];
         const ParamDesc d = pdesc[tile.param];
@@ -196,20 +230,20 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
         const int64_t ke = min(kb + TILE, d.span);
         const int64_t re = min(ke, L);
         float *__restrict__ o = out + d.off;
-        const uint16_t *const *__restrict__ P = ptrs + static_cast<int64_t>(tile.param) * N;
+        const char *const *__restrict__ P = ptrs + static_cast<int64_t>(tile.param) * N;
 
         if (kb < re) {
             int64_t vs = re, ve = re;
             if (vec_in) {
-                vs = min(re, kb + ((VEC - ((src + kb) & (VEC - 1))) & (VEC - 1)));
-                ve = vs + ((re - vs) & ~static_cast<int64_t>(VEC - 1));
+                vs = min(re, kb + ((4 - ((src + kb) & 3)) & 3));
+                ve = vs + ((re - vs) & ~static_cast<int64_t>(3));
             }
-            rs_elems<BLOCK>(P, N, src, o, kb, vs);
-            rs_elems<BLOCK>(P, N, src, o, ve, re);
+            rs_elems<IT, BLOCK>(P, N, avg, src, o, kb, vs);
+            rs_elems<IT, BLOCK>(P, N, avg, src, o, ve, re);
 
-            // A tile holds at most TILE/VEC chunks, so every per-lane byte
+            // A tile holds at most TILE/4 chunks, so every per-lane byte
             // offset below fits in 32 bits.
-            const int nch = static_cast<int>((ve - vs) / VEC);
+            const int nch = static_cast<int>((ve - vs) >> 2);
             const bool st16 = vec_out && (((d.off + vs) & 3) == 0);
             GLOBAL_AS char *obase = gstore_ptr<char>(o + vs);
             for (int c0 = 0; c0 < nch; c0 += BLOCK * CPL) {
@@ -222,27 +256,29 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
                     // Lanes past the end re-read the last chunk (in bounds)
                     // and do not store.
                     const uint32_t c = static_cast<uint32_t>(ok[j] ? ch : nch - 1);
-                    in_off[j] = c * (2u * VEC);
-                    out_off[j] = c * (4u * VEC);
+                    in_off[j] = c * (4u * ES);
+                    out_off[j] = c * 16u;
                 }
-                f32x4 acc[CPL][VEC / 4];
-                rs_batch<CPL, VEC, RB, true>(P, 0, min(N, RB), src + vs, in_off, acc);
+                f32x4 acc[CPL];
+                const int64_t first_byte = (src + vs) * ES;
+                rs_batch<IT, CPL, RB, true>(P, 0, min(N, RB), first_byte, in_off, acc);
                 for (int r0 = RB; r0 < N; r0 += RB)
-                    rs_batch<CPL, VEC, RB, false>(P, r0, min(N - r0, RB), src + vs, in_off, acc);
+                    rs_batch<IT, CPL, RB, false>(P, r0, min(N - r0, RB), first_byte, in_off, acc);
+                if (avg) {
+                    const float n = static_cast<float>(N);
+#pragma unroll
+                    for (int j = 0; j < CPL; j++)
+                        acc[j] = f32x4{acc[j].x / n, acc[j].y / n, acc[j].z / n, acc[j].w / n};
+                }
 #pragma unroll
                 for (int j = 0; j < CPL; j++) {
                     if (!ok[j]) continue;
                     if (st16) {
-                        GLOBAL_AS f32x4 *dst =
-                            reinterpret_cast<GLOBAL_AS f32x4 *>(obase + out_off[j]);
-#pragma unroll
-                        for (int h = 0; h < VEC / 4; h++) stream_store(acc[j][h], dst + h);
+                        stream_store(acc[j], reinterpret_cast<GLOBAL_AS f32x4 *>(obase + out_off[j]));
                     } else {
                         GLOBAL_AS float *dst = reinterpret_cast<GLOBAL_AS float *>(obase + out_off[j]);
 #pragma unroll
-                        for (int h = 0; h < VEC / 4; h++)
-#pragma unroll
-                            for (int e = 0; e < 4; e++) dst[4 * h + e] = acc[j][h][e];
+                        for (int e = 0; e < 4; e++) dst[e] = acc[j][e];
                     }
                 }
             }
@@ -353,9 +389,6 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
 #ifndef TIDE_RS_CPL
 #define TIDE_RS_CPL 4
 #endif
-#ifndef TIDE_RS_VEC
-#define TIDE_RS_VEC 4
-#endif
 #ifndef TIDE_DEFAULT_ONE_TILE_PER_WG
 #define TIDE_DEFAULT_ONE_TILE_PER_WG 1
 #endif
@@ -376,9 +409,6 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
 #endif
 #ifndef TIDE_SMALL_CPL
 #define TIDE_SMALL_CPL 2
-#endif
-#ifndef TIDE_SMALL_VEC
-#define TIDE_SMALL_VEC 4
 #endif
 #ifndef TIDE_SMALL_RB
 #define TIDE_SMALL_RB 16
@@ -611,6 +641,36 @@ tide_status allow_lds(const void *kernel, int bytes) {
     return TIDE_OK;
 }
 
+// Everything one tide_rs launch needs.
+struct RsLaunch {
+    const ParamDesc *pd;
+    const Tile *tiles;
+    int64_t ntiles;
+    const char *const *ptrs;
+    int N, R, avg;
+    float *out;
+    int vec_in, vec_out;
+    unsigned grid;
+    int lds;
+    hipStream_t stream;
+};
+
+// Default launches: one 256-lane workgroup per 4096-element tile, at most
+// TIDE_RS_WG_CAP per CU.  Small-footprint launches: the small tile list and
+// its kernel shape, at most one workgroup per CU.
+template <int IT, bool SMALL>
+tide_status launch_rs(const RsLaunch &a) {
+    auto k = SMALL ? rs_kernel<IT, TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_RB, TIDE_SMALL_PACE,
+                               TIDE_XMAP_RS, kRsTileSmall>
+                   : rs_kernel<IT, kBlock, kRsChunksPerLane, TIDE_RS_RB, 0, TIDE_XMAP_RS, kRsTile>;
+    tide_status st = allow_lds(reinterpret_cast<const void *>(k), a.lds);
+    if (st != TIDE_OK) return st;
+    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_BLOCK : kBlock), a.lds, a.stream,
+                       a.pd, a.tiles, a.ntiles, a.ptrs, a.N, a.R, a.avg, a.out, a.vec_in,
+                       a.vec_out);
+    return TIDE_OK;
+}
+
 }  // namespace
 
 void release_device_states(const tide_plan *p) {
@@ -662,31 +722,28 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
     const int64_t ntiles =
         static_cast<int64_t>(small ? plan->rs_tiles_small.size() : plan->rs_tiles.size());
-    const unsigned grid = tide::grid_size(ds, ntiles, flags, max_workgroups);
-    const int vec_in = pt->aligned16 ? 1 : 0;
-    const int vec_out = (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0;
+    const tide::RsLaunch L{static_cast<const tide::ParamDesc *>(ds->d_params),
+                           static_cast<const tide::Tile *>(small ? ds->d_rs_tiles_small
+                                                                 : ds->d_rs_tiles),
+                           ntiles,
+                           static_cast<const char *const *>(pt->dev),
+                           plan->N,
+                           rank,
+                           (flags & TIDE_F_AVG) ? 1 : 0,
+                           out,
+                           pt->aligned16 ? 1 : 0,
+                           (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
+                           tide::grid_size(ds, ntiles, flags, max_workgroups),
+                           small ? ds->small_lds : ds->rs_cap_lds,
+                           static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
-    const auto *pd = static_cast<const tide::ParamDesc *>(ds->d_params);
-    const auto *gp = static_cast<const uint16_t *const *>(pt->dev);
-    if (small) {
-        auto k = tide::rs_kernel<TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_VEC, TIDE_SMALL_RB,
-                                 TIDE_SMALL_PACE, TIDE_XMAP_RS, tide::kRsTileSmall>;
-        st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->small_lds);
-        if (st != TIDE_OK) return st;
-        hipLaunchKernelGGL(k, dim3(grid), dim3(TIDE_SMALL_BLOCK), ds->small_lds,
-                           static_cast<hipStream_t>(stream), pd,
-                           static_cast<const tide::Tile *>(ds->d_rs_tiles_small), ntiles, gp,
-                           plan->N, rank, out, vec_in, vec_out);
-    } else {
-        auto k = tide::rs_kernel<tide::kBlock, tide::kRsChunksPerLane, TIDE_RS_VEC, TIDE_RS_RB, 0,
-                                 TIDE_XMAP_RS, tide::kRsTile>;
-        st = tide::allow_lds(reinterpret_cast<const void *>(k), ds->rs_cap_lds);
-        if (st != TIDE_OK) return st;
-        hipLaunchKernelGGL(k, dim3(grid), dim3(tide::kBlock), ds->rs_cap_lds,
-                           static_cast<hipStream_t>(stream), pd,
-                           static_cast<const tide::Tile *>(ds->d_rs_tiles), ntiles, gp, plan->N,
-                           rank, out, vec_in, vec_out);
-    }
+    if (flags & TIDE_F_GRAD_F32)
+        st = small ? tide::launch_rs<tide::kF32, true>(L) : tide::launch_rs<tide::kF32, false>(L);
+    else if (flags & TIDE_F_GRAD_F16)
+        st = small ? tide::launch_rs<tide::kF16, true>(L) : tide::launch_rs<tide::kF16, false>(L);
+    else
+        st = small ? tide::launch_rs<tide::kBf16, true>(L) : tide::launch_rs<tide::kBf16, false>(L);
+    if (st != TIDE_OK) return st;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
     tide::clear_error();

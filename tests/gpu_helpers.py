@@ -64,5 +64,6 @@ def first_mismatch(got, want):
 
 
 def run_rs(plan, R, grads_or_table, out, **kw):
+    """tide_rs, then wait for it."""
     tide.rs(plan, R, grads_or_table, out, **kw)
     torch.cuda.synchronize()

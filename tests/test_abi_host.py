@@ -127,7 +127,6 @@ def test_rs_argument_errors():
     assert _rs(plan, -1, good, out) == E_INVALID
     assert _rs(plan, 0, good, out, flags=0x2) == E_UNSUPPORTED   # copy engine: AG only
     assert b"tide_ag" in L.tide_last_error()
-    assert _rs(plan, 0, good, out, flags=0x4) == E_UNSUPPORTED
     assert _rs(plan, 0, good, out, max_wg=-1) == E_INVALID
     assert _rs(plan, 0, None, out) == E_INVALID and b"grads" in L.tide_last_error()
     assert _rs(plan, 0, good, 0) == E_INVALID and b"out is NULL" in L.tide_last_error()
@@ -137,6 +136,16 @@ def test_rs_argument_errors():
     # out overlaps what rank 0 reads of rank 1's first gradient (elements 0..7)
     assert _rs(plan, 0, good, A + 0x20000 + 8) == E_INVALID
     assert b"overlaps" in L.tide_last_error()
+    # gradient element types: both type flags, fp32 pointers 2- but not 4-aligned
+    assert _rs(plan, 0, good, out, flags=0x18) == E_INVALID
+    assert b"both" in L.tide_last_error()
+    assert _rs(plan, 0, _ptrs([A, A + 0x10002, A + 0x20000, A + 0x30000]), out,
+               flags=0x10) == E_INVALID
+    assert b"element size" in L.tide_last_error()
+    # fp32 gradients read 4 bytes per element: out at 16 bytes into rank 1's
+    # first gradient overlaps elements 4..7 only when they are 4 bytes wide
+    assert _rs(plan, 0, good, A + 0x20000 + 16, flags=0x10) == E_INVALID
+    assert _rs(plan, 0, good, out, flags=0x20) == E_UNSUPPORTED
 
 
 def test_rs_empty_plan_is_a_noop():
@@ -185,6 +194,9 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         tide.grad_table(plan, cpu)                   # not device tensors
     with pytest.raises(TypeError):
-        tide.grad_table(plan, [[torch.zeros(4, 4)] for _ in range(2)])
+        tide.grad_table(plan, [[torch.zeros(4, 4, dtype=torch.int32)] for _ in range(2)])
+    with pytest.raises(TypeError):   # one dtype for all gradients
+        tide.grad_table(plan, [[torch.zeros(4, 4, dtype=torch.bfloat16)],
+                               [torch.zeros(4, 4, dtype=torch.float16)]])
     with pytest.raises(ValueError):
         tide.grad_table(plan, cpu[:1])

@@ -199,6 +199,89 @@ def test_deterministic_and_streams(orc):
 
 
 # ---------------------------------------------------------------------------
+# gradient element types and the mean
+# ---------------------------------------------------------------------------
+
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def typed_grads(shapes, N, seed, dtype):
+    g = workloads.random_grads_for_shapes(shapes, N, seed_base=seed)
+    return [[t.float().to(_TORCH[dtype]).to(DEV) for t in rank] for rank in g]
+
+
+def host_elems(t, dtype):
+    t = t.detach().contiguous().cpu()
+    return t.numpy() if dtype == "f32" else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def check_rs_typed(orc, shapes, N, grads, R, dtype, avg, align=1, **kw):
+    plan = tide.Plan(shapes, N, align)
+    out = fresh_out(plan.S)
+    note(f"tide_rs typed {dtype} avg={avg} shapes={shapes} N={N} R={R} {kw}")
+    run_rs(plan, R, grads, out, avg=avg, **kw)
+    slices = [[host_elems(g.reshape(-1)[plan.real(R, i)[0]:plan.real(R, i)[0] +
+                                        plan.real(R, i)[1]], dtype)
+               for i, g in enumerate(rank)] for rank in grads]
+    want = orc.rs_slices(shapes, N, R, slices, align=align, dtype=dtype, avg=avg)
+    got = out.cpu().numpy()
+    assert same_f32(got, want), (dtype, avg, R, first_mismatch(got, want))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("N", [1, 3, 8, 16])
+def test_typed_and_mean(orc, dtype, N):
+    shapes = RAGGED[0]
+    g = typed_grads(shapes, N, 300 + N, dtype)
+    for R in sorted({0, N // 2, N - 1}):
+        for avg in (False, True):
+            check_rs_typed(orc, shapes, N, g, R, dtype, avg)
+        check_rs_typed(orc, shapes, N, g, R, dtype, True, small=True)
+
+
+def test_typed_unaligned_and_gaps(orc):
+    """fp16/fp32 gradients at odd element offsets (scalar path) and with
+    alignment gaps in the block."""
+    shapes = [(513, 5), (4100,), (7, 3)]
+    N = 4
+    for dtype in ("f16", "f32"):
+        base = typed_grads(shapes, N, 77, dtype)
+        grads = []
+        for r, rank in enumerate(base):
+            row = []
+            for i, t in enumerate(rank):
+                n = t.numel()
+                buf = torch.zeros(n + 8, dtype=t.dtype, device=DEV)
+                shift = (r + i) % 3 + 1
+                buf[shift:shift + n].copy_(t.reshape(-1))
+                row.append(buf[shift:shift + n].view(t.shape))
+            grads.append(row)
+        for R in range(N):
+            check_rs_typed(orc, shapes, N, grads, R, dtype, R % 2 == 1)
+        for R in range(N):
+            check_rs_typed(orc, shapes, N, base, R, dtype, False, align=6)
+
+
+def test_f16_special_values(orc):
+    """fp16 subnormals, -0.0, +-Inf and NaN through the vector path."""
+    N = 4
+    n = 4096 + 40
+    pool = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x0400, 0x7BFF, 0xFBFF, 0x7C00,
+                     0xFC00, 0x7E00, 0x3C00, 0xBC00], np.uint16)
+    rng = np.random.default_rng(5)
+    grads = []
+    for r in range(N):
+        bits = pool[rng.integers(0, len(pool), size=n)]
+        bits[:64] = 0x8000
+        bits[64:128] = 0x0001           # 2^-24: sums exact in fp32
+        grads.append([torch.from_numpy(bits.view(np.int16)).view(torch.float16).to(DEV)
+                      .reshape(n // 4, 4)])
+    for R in range(N):
+        for avg in (False, True):
+            check_rs_typed(orc, [(n // 4, 4)], N, grads, R, "f16", avg)
+
+
+# ---------------------------------------------------------------------------
 # all-gather placement
 # ---------------------------------------------------------------------------
 
