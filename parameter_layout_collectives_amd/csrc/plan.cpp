@@ -29,27 +29,26 @@ namespace tide {
 namespace {
 thread_local std::string g_last_error;
 
-// One half-open byte interval that a call reads (dst = false) or writes.
+// One half-open byte interval [lo, hi).
 struct Span {
     uintptr_t lo, hi;
-    bool dst;
 };
 
-// True if some written span overlaps any other span.
-bool written_overlaps(std::vector<Span> &v) {
-    std::sort(v.begin(), v.end(), [](const Span &a, const Span &b) { return a.lo < b.lo; });
-    uintptr_t max_any = 0, max_dst = 0;
-    bool have = false;
-    for (const Span &s : v) {
-        if (have) {
-            if (s.dst && s.lo < max_any) return true;
-            if (!s.dst && s.lo < max_dst) return true;
-        }
-        max_any = std::max(max_any, s.hi);
-        if (s.dst) max_dst = std::max(max_dst, s.hi);
-        have = true;
-    }
-    return false;
+bool overlap(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Sorts `dst` and reports whether two of its spans overlap.
+bool sort_and_check_disjoint(std::vector<Span> &dst) {
+    std::sort(dst.begin(), dst.end(), [](const Span &a, const Span &b) { return a.lo < b.lo; });
+    for (size_t k = 1; k < dst.size(); k++)
+        if (dst[k].lo < dst[k - 1].hi) return false;
+    return true;
+}
+
+// True if `s` overlaps a span of `dst` (sorted, disjoint: hi ascends too).
+bool hits_sorted(const std::vector<Span> &dst, const Span &s) {
+    auto it = std::upper_bound(dst.begin(), dst.end(), s.lo,
+                               [](uintptr_t v, const Span &d) { return v < d.hi; });
+    return it != dst.end() && it->lo < s.hi;
 }
 }  // namespace
 
@@ -82,10 +81,10 @@ tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *g
     if (!out) return fail(TIDE_E_INVALID, "tide_rs: out is NULL");
     if (reinterpret_cast<uintptr_t>(out) & 3)
         return fail(TIDE_E_INVALID, "tide_rs: out is not 4-byte aligned");
-    std::vector<Span> spans;
-    spans.reserve(static_cast<size_t>(p->N) * p->P + 1);
+    // One pass over the N*P gradient runs rank `rank` reads (no allocation):
+    // each must be non-null, element-aligned and disjoint from `out`.
     const uintptr_t o = reinterpret_cast<uintptr_t>(out);
-    spans.push_back({o, o + static_cast<uintptr_t>(p->S) * 4u, true});
+    const Span written{o, o + static_cast<uintptr_t>(p->S) * 4u};
     for (int32_t i = 0; i < p->P; i++) {
         int64_t src, L;
         shard_run(p, rank, i, &src, &L);
@@ -100,12 +99,12 @@ tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *g
                 return fail(TIDE_E_INVALID, "tide_rs: grads[" + std::to_string(r) + "*P+" +
                                                 std::to_string(i) +
                                                 "] is not aligned to its element size");
-            spans.push_back({a + static_cast<uintptr_t>(src) * es,
-                             a + static_cast<uintptr_t>(src + L) * es, false});
+            const Span read{a + static_cast<uintptr_t>(src) * es,
+                            a + static_cast<uintptr_t>(src + L) * es};
+            if (overlap(read, written))
+                return fail(TIDE_E_INVALID, "tide_rs: out overlaps gradient elements it would read");
         }
     }
-    if (written_overlaps(spans))
-        return fail(TIDE_E_INVALID, "tide_rs: out overlaps gradient elements it would read");
     return TIDE_OK;
 }
 
@@ -125,8 +124,11 @@ tide_status check_ag_args(const tide_plan *p, const void *const *rank_src,
     if (!rank_src) return fail(TIDE_E_INVALID, "tide_ag: rank_src array is NULL");
     if (!params) return fail(TIDE_E_INVALID, "tide_ag: params array is NULL");
     const uintptr_t e = static_cast<uintptr_t>(elem_bytes);
-    std::vector<Span> spans;
-    spans.reserve(static_cast<size_t>(p->N + 1) * p->P);
+    // Destinations: sorted once (P log P) and checked pairwise disjoint.  A
+    // rank block is then checked against them whole, and run by run (binary
+    // searches) only if it touches one: padding may lie under a destination.
+    thread_local std::vector<Span> dst;
+    dst.clear();
     for (int32_t i = 0; i < p->P; i++) {
         if (p->numel[i] == 0) continue;
         const uintptr_t d = reinterpret_cast<uintptr_t>(params[i]);
@@ -135,29 +137,36 @@ tide_status check_ag_args(const tide_plan *p, const void *const *rank_src,
         if (d % e)
             return fail(TIDE_E_INVALID, "tide_ag: params[" + std::to_string(i) +
                                             "] is not aligned to its element size");
-        spans.push_back({d, d + static_cast<uintptr_t>(p->numel[i]) * e, true});
+        dst.push_back({d, d + static_cast<uintptr_t>(p->numel[i]) * e});
     }
+    if (!sort_and_check_disjoint(dst))
+        return fail(TIDE_E_INVALID, "tide_ag: a destination overlaps another destination");
+    const uintptr_t block_bytes = static_cast<uintptr_t>(p->S) * e;
     for (int32_t r = 0; r < p->N; r++) {
         const uintptr_t s = reinterpret_cast<uintptr_t>(rank_src[r]);
-        bool used = false;
+        // A rank block that no destination touches needs no per-run check.
+        if (s && s % e == 0 && !hits_sorted(dst, Span{s, s + block_bytes})) continue;
+        bool checked = false;
         for (int32_t i = 0; i < p->P; i++) {
             int64_t src, L;
             shard_run(p, r, i, &src, &L);
             if (L == 0) continue;
-            used = true;
-            spans.push_back({s + static_cast<uintptr_t>(p->off[i]) * e,
-                             s + static_cast<uintptr_t>(p->off[i] + L) * e, false});
+            if (!checked) {
+                if (!s)
+                    return fail(TIDE_E_INVALID,
+                                "tide_ag: rank_src[" + std::to_string(r) + "] is NULL");
+                if (s % e)
+                    return fail(TIDE_E_INVALID, "tide_ag: rank_src[" + std::to_string(r) +
+                                                    "] is not aligned to its element size");
+                checked = true;
+            }
+            const Span read{s + static_cast<uintptr_t>(p->off[i]) * e,
+                            s + static_cast<uintptr_t>(p->off[i] + L) * e};
+            if (hits_sorted(dst, read))
+                return fail(TIDE_E_INVALID,
+                            "tide_ag: a destination overlaps a source element that is read");
         }
-        if (!used) continue;
-        if (!s)
-            return fail(TIDE_E_INVALID, "tide_ag: rank_src[" + std::to_string(r) + "] is NULL");
-        if (s % e)
-            return fail(TIDE_E_INVALID, "tide_ag: rank_src[" + std::to_string(r) +
-                                            "] is not aligned to its element size");
     }
-    if (written_overlaps(spans))
-        return fail(TIDE_E_INVALID,
-                    "tide_ag: a destination overlaps another destination or a source element");
     return TIDE_OK;
 }
 

@@ -556,8 +556,7 @@ tide_status device_state(const tide_plan *p, DeviceState **out) {
     return TIDE_OK;
 }
 
-uint64_t hash_ptrs(const uintptr_t *v, size_t n) {
-    uint64_t h = 1469598103934665603ull;
+uint64_t hash_ptrs(uint64_t h, const uintptr_t *v, size_t n) {
     for (size_t i = 0; i < n; i++) {
         h ^= static_cast<uint64_t>(v[i]);
         h *= 1099511628211ull;
@@ -565,15 +564,30 @@ uint64_t hash_ptrs(const uintptr_t *v, size_t n) {
     return h;
 }
 
-// Finds (or uploads) the device copy of a pointer array.  `dev_order` is
-// the array as the kernel wants it (it may be a permutation of `key`).
-// Caller holds p->mu.
-tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache,
-                          const std::vector<uintptr_t> &key,
-                          const std::vector<uintptr_t> &dev_order, PtrTable **out) {
-    const uint64_t h = hash_ptrs(key.data(), key.size());
+// A pointer set as the caller passed it: `na` entries at `a`, then `nb` at
+// `b` (read in place; copied only when a new table is made).
+struct PtrKey {
+    const uintptr_t *a;
+    size_t na;
+    const uintptr_t *b;
+    size_t nb;
+    size_t size() const { return na + nb; }
+    bool equals(const std::vector<uintptr_t> &k) const {
+        return k.size() == size() && std::memcmp(k.data(), a, na * sizeof(uintptr_t)) == 0 &&
+               (nb == 0 || std::memcmp(k.data() + na, b, nb * sizeof(uintptr_t)) == 0);
+    }
+};
+
+// Finds (or uploads) the device copy of a pointer set.  A hit costs one hash
+// and one compare over the caller's arrays.  On a miss `order(key, dev)`
+// writes the array as the kernel wants it (`dev_len` entries: a permutation
+// of the key, possibly padded) and it is uploaded.  Caller holds p->mu.
+template <typename Order>
+tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const PtrKey &key,
+                          size_t dev_len, Order order, PtrTable **out) {
+    const uint64_t h = hash_ptrs(hash_ptrs(1469598103934665603ull, key.a, key.na), key.b, key.nb);
     for (auto &pt : cache)
-        if (pt.hash == h && pt.key == key) {
+        if (pt.hash == h && key.equals(pt.key)) {
             pt.last_use = ++ds->tick;
             *out = &pt;
             return TIDE_OK;
@@ -590,16 +604,20 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache,
         cache.erase(lru);
     }
     PtrTable pt;
+    std::vector<uintptr_t> dev;
     try {
-        pt.key = key;
+        pt.key.resize(key.size());
+        dev.assign(dev_len, 0);
     } catch (const std::bad_alloc &) {
         return fail(TIDE_E_NOMEM, "pointer table: out of host memory");
     }
+    std::copy(key.a, key.a + key.na, pt.key.begin());
+    if (key.nb) std::copy(key.b, key.b + key.nb, pt.key.begin() + key.na);
+    order(pt.key.data(), dev.data());
     pt.hash = h;
     pt.aligned16 = true;
-    for (uintptr_t a : key) pt.aligned16 = pt.aligned16 && (a & 15) == 0;
-    tide_status st = upload(dev_order.data(), dev_order.size() * sizeof(uintptr_t), &pt.dev,
-                            "pointer table");
+    for (uintptr_t a : pt.key) pt.aligned16 = pt.aligned16 && (a & 15) == 0;
+    tide_status st = upload(dev.data(), dev.size() * sizeof(uintptr_t), &pt.dev, "pointer table");
     if (st != TIDE_OK) return st;
     pt.last_use = ++ds->tick;
     try {
@@ -696,27 +714,23 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
     if (st != TIDE_OK) return st;
     if (plan->S == 0) return TIDE_OK;
 
-    const size_t n = static_cast<size_t>(plan->N) * plan->P;
-    std::vector<uintptr_t> key, dev_order;
-    try {
-        key.assign(reinterpret_cast<const uintptr_t *>(grads),
-                   reinterpret_cast<const uintptr_t *>(grads) + n);
-        dev_order.resize(n);
-        dev_order.reserve(n + tide::kPtrPad);
-    } catch (const std::bad_alloc &) {
-        return fail(TIDE_E_NOMEM, "tide_rs: out of host memory");
-    }
-    for (int32_t r = 0; r < plan->N; r++)
-        for (int32_t i = 0; i < plan->P; i++)
-            dev_order[static_cast<size_t>(i) * plan->N + r] = key[static_cast<size_t>(r) * plan->P + i];
-    dev_order.insert(dev_order.end(), tide::kPtrPad, 0);
+    // The kernel reads the table parameter-major (entry i*N + r), followed by
+    // kPtrPad null entries so that a batch's pointers load in one scalar load.
+    const int32_t N = plan->N, P = plan->P;
+    const tide::PtrKey key{reinterpret_cast<const uintptr_t *>(grads),
+                           static_cast<size_t>(N) * P, nullptr, 0};
+    auto param_major = [N, P](const uintptr_t *k, uintptr_t *dev) {
+        for (int32_t r = 0; r < N; r++)
+            for (int32_t i = 0; i < P; i++)
+                dev[static_cast<size_t>(i) * N + r] = k[static_cast<size_t>(r) * P + i];
+    };
 
     std::lock_guard<std::mutex> lock(plan->mu);
     tide::DeviceState *ds = nullptr;
     st = tide::device_state(plan, &ds);
     if (st != TIDE_OK) return st;
     tide::PtrTable *pt = nullptr;
-    st = tide::pointer_table(ds, ds->rs_cache, key, dev_order, &pt);
+    st = tide::pointer_table(ds, ds->rs_cache, key, key.size() + tide::kPtrPad, param_major, &pt);
     if (st != TIDE_OK) return st;
 
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
@@ -826,21 +840,20 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
         return st;
     }
 
-    std::vector<uintptr_t> key;
-    try {
-        key.reserve(static_cast<size_t>(plan->N) + plan->P);
-        for (int32_t r = 0; r < plan->N; r++) key.push_back(reinterpret_cast<uintptr_t>(rank_src[r]));
-        for (int32_t i = 0; i < plan->P; i++) key.push_back(reinterpret_cast<uintptr_t>(params[i]));
-    } catch (const std::bad_alloc &) {
-        return fail(TIDE_E_NOMEM, "tide_ag: out of host memory");
-    }
+    // Table: the N rank block pointers, then the P parameter pointers.
+    const tide::PtrKey key{reinterpret_cast<const uintptr_t *>(rank_src),
+                           static_cast<size_t>(plan->N),
+                           reinterpret_cast<const uintptr_t *>(params),
+                           static_cast<size_t>(plan->P)};
+    const size_t n = key.size();
+    auto as_is = [n](const uintptr_t *k, uintptr_t *dev) { std::copy(k, k + n, dev); };
 
     std::lock_guard<std::mutex> lock(plan->mu);
     tide::DeviceState *ds = nullptr;
     st = tide::device_state(plan, &ds);
     if (st != TIDE_OK) return st;
     tide::PtrTable *pt = nullptr;
-    st = tide::pointer_table(ds, ds->ag_cache, key, key, &pt);
+    st = tide::pointer_table(ds, ds->ag_cache, key, n, as_is, &pt);
     if (st != TIDE_OK) return st;
 
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;

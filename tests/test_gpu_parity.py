@@ -385,6 +385,49 @@ def test_ag_inverts_rs_layout(orc):
         assert np.array_equal(bits32(params[i]).reshape(-1), want[i]), i
 
 
+def test_ag_destinations_inside_unread_parts_of_blocks(orc):
+    """Destinations may lie in the gaps of the gathered buffer, which are
+    never read: the call is accepted and every read element is placed."""
+    shapes = [(3, 4), (5,)]
+    N, align = 2, 64          # S = 128; rank blocks read [0,8), [64,67) / [0,4), [64,66)
+    plan = tide.Plan(shapes, N, align)
+    assert plan.S == 128
+    rng = np.random.default_rng(77)
+    host = rng.integers(0, 65535, size=N * plan.S).astype(np.uint16)
+    gathered = torch.from_numpy(host.view(np.int16)).to(DEV).view(torch.bfloat16)
+    blocks = [gathered[r * plan.S:(r + 1) * plan.S] for r in range(N)]
+    params = [gathered[plan.S + 10:plan.S + 22].view(3, 4),   # in rank 1's gap [8, 64)
+              gathered[16:21]]                                # in rank 0's gap
+    note("tide_ag destinations inside block gaps")
+    tide.ag(plan, blocks, params)
+    torch.cuda.synchronize()
+    want = orc.ag(shapes, N, [host[r * plan.S:(r + 1) * plan.S] for r in range(N)],
+                  elem_bytes=2, align=align)
+    got_all = bits16(gathered)
+    for i, p in enumerate(params):
+        assert np.array_equal(bits16(p).reshape(-1), want[i]), i
+    untouched = np.ones(N * plan.S, bool)
+    untouched[plan.S + 10:plan.S + 22] = False
+    untouched[16:21] = False
+    assert np.array_equal(got_all[untouched], host[untouched])
+
+
+def test_rs_output_inside_unread_rows_of_a_gradient(orc):
+    """`out` may overlap gradient elements the call does not read (rows of
+    other ranks' shards)."""
+    shapes = [(256, 4), (10,)]
+    N, R = 4, 3               # rank 3 reads rows 192..255 of param 0, element 9 of param 1
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=55))
+    plan = tide.Plan(shapes, N)
+    assert plan.S == 259
+    out = g[1][0].reshape(-1)[0:2 * plan.S].view(torch.float32)   # rank 1's rows 0..129
+    note("tide_rs out inside unread gradient rows")
+    run_rs(plan, R, g, out)
+    want = expected_rs(orc, shapes, N, R, g, plan)
+    got = out.cpu().numpy()
+    assert same_f32(got, want), first_mismatch(got, want)
+
+
 # ---------------------------------------------------------------------------
 # runtime behaviour
 # ---------------------------------------------------------------------------
