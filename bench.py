@@ -47,7 +47,10 @@ import parameter_layout_collectives_amd as tide  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "parameter_layout_collectives_amd", "csrc", "tide_kernels.hip")
+# The kernels' machine code depends on these two files only (the runtime and
+# the plan code around them do not change what a launch executes).
+KERNEL_SRCS = [os.path.join(ROOT, "parameter_layout_collectives_amd", "csrc", f)
+               for f in ("kernels.hip", "kernel_abi.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama31_70b_layer.json")
 
 
@@ -60,8 +63,11 @@ def fmt(x):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def rs_bytes(plan, R):

@@ -46,8 +46,14 @@
  *
  * Streams.  tide_rs and tide_ag are asynchronous and stream-ordered on the
  * given hipStream_t (passed as void*; NULL = the null stream).  The first
- * call of a plan on a device, and a call with a pointer set the plan has not
- * seen recently, upload small tables with blocking copies before launching.
+ * call of a plan on a device uploads its geometry tables with blocking
+ * copies.  Device pointer tables are cached per plan and device (8 pointer
+ * sets per operation, least recently used replaced): a set already cached
+ * costs a hash and a compare on the host and no upload; a new set is copied
+ * through a pinned staging buffer by an async copy on the call's stream.
+ * Replacing a set waits (on the host) until the launches that read it have
+ * finished.  A call on another stream that hits a set whose upload may still
+ * be in flight makes its stream wait for that upload.
  */
 #ifndef TIDE_H
 #define TIDE_H

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtide.so")
 
-SOURCES = ["plan.cpp", "tide_kernels.hip"]
+SOURCES = ["plan.cpp", "runtime.hip", "kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -11,60 +11,26 @@
 #include <vector>
 
 #include "../../include/tide.h"
+#include "kernel_abi.h"
 
 namespace tide {
 
-// Build-time tuning constants (defaults are the measured best on MI355X).
-#ifndef TIDE_RS_TILE
-#define TIDE_RS_TILE 4096
-#endif
-#ifndef TIDE_AG_TILE
-#define TIDE_AG_TILE 2048
-#endif
-#ifndef TIDE_AG_TILE_SMALL
-#define TIDE_AG_TILE_SMALL 16384
-#endif
-#ifndef TIDE_RS_TILE_SMALL
-#define TIDE_RS_TILE_SMALL 2048
-#endif
-
-// Elements of one parameter segment handled by one reduce-scatter tile, and
-// by one all-gather tile.  Both are multiples of 8 so that tile starts keep
-// the 16-byte phase of the segment they cut.
-constexpr int64_t kRsTile = TIDE_RS_TILE;
-constexpr int64_t kAgTile = TIDE_AG_TILE;
-// Small-footprint all-gather launches keep one workgroup per CU resident, so
-// each one moves a larger tile to keep enough bytes in flight.
-constexpr int64_t kAgTileSmall = TIDE_AG_TILE_SMALL;
-constexpr int64_t kRsTileSmall = TIDE_RS_TILE_SMALL;
-static_assert(kRsTile % 8 == 0 && kAgTile % 8 == 0 && kAgTileSmall % 8 == 0 &&
-                  kRsTileSmall % 8 == 0,
-              "tiles must keep the 16-byte phase");
-static_assert(kAgTileSmall * 4 < (int64_t(1) << 31), "all-gather tile bytes must fit in int");
-constexpr int kBlock = 256;           // lanes per workgroup (4 wave64)
-
-// Per-parameter geometry as the kernels read it.  src(r) = r*seg and
-// L(r) = min(seg, max(0, numel - r*seg)) follow from seg and numel.
-struct ParamDesc {
-    int64_t off;     // offset of the parameter's segment in a rank block
-    int64_t seg;     // c * inner: elements per rank block (padding included)
-    int64_t numel;   // dim0 * inner: elements of the full tensor
-    int64_t span;    // seg plus the alignment gap up to the next offset (or S)
-};
-
-// One tile: `param`'s elements [k0, k0 + tile) of rank `rank`'s segment
-// (all-gather) or of the parameter's span in the block (reduce-scatter,
-// where `rank` is unused: the rank is a launch argument).
-struct Tile {
-    int32_t param;
-    int32_t rank;
-    int64_t k0;
-};
-
+// One slot of a plan's pointer-table cache on one device.  A slot's buffers
+// are allocated once and reused for every pointer set it holds: a new set
+// is written to the pinned staging copy and uploaded with an async copy on
+// the caller's stream, so the launch that follows reads it in stream order.
 struct PtrTable {
     std::vector<uintptr_t> key;  // the host pointer array it was built from
     uint64_t hash = 0;
     void *dev = nullptr;         // device copy of the pointer array
+    void *staging = nullptr;     // pinned host buffer the upload reads
+    void *done = nullptr;        // hipEvent_t recorded after the last launch that read `dev`
+    void *last_stream = nullptr; // stream of that launch
+    bool recorded = false;       // `done` has been recorded at least once
+    bool many_streams = false;   // read on more than one stream since the last upload
+    void *uploaded = nullptr;    // hipEvent_t recorded after the upload of the current set
+    void *upload_stream = nullptr;
+    bool upload_done = false;    // the upload is known to have finished
     bool aligned16 = false;      // every non-null pointer is 16-byte aligned
     uint64_t last_use = 0;
 };

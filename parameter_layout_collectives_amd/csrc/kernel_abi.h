@@ -1,0 +1,143 @@
+// What the TIDE kernels read and how they are launched: table formats, tile
+// sizes, kernel shapes and the launch descriptors.  The kernels and their
+// launch functions live in kernels.hip; the runtime (runtime.hip) builds the
+// tables and calls the launch functions.  Nothing here changes without
+// changing the kernels' machine code.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace tide {
+
+// Build-time tuning constants (defaults are the measured best on MI355X).
+#ifndef TIDE_RS_TILE
+#define TIDE_RS_TILE 4096
+#endif
+#ifndef TIDE_AG_TILE
+#define TIDE_AG_TILE 2048
+#endif
+#ifndef TIDE_AG_TILE_SMALL
+#define TIDE_AG_TILE_SMALL 16384
+#endif
+#ifndef TIDE_RS_TILE_SMALL
+#define TIDE_RS_TILE_SMALL 2048
+#endif
+
+// Elements of one parameter segment handled by one reduce-scatter tile, and
+// by one all-gather tile.  Both are multiples of 8 so that tile starts keep
+// the 16-byte phase of the segment they cut.
+constexpr int64_t kRsTile = TIDE_RS_TILE;
+constexpr int64_t kAgTile = TIDE_AG_TILE;
+// Small-footprint all-gather launches keep one workgroup per CU resident, so
+// each one moves a larger tile to keep enough bytes in flight.
+constexpr int64_t kAgTileSmall = TIDE_AG_TILE_SMALL;
+constexpr int64_t kRsTileSmall = TIDE_RS_TILE_SMALL;
+static_assert(kRsTile % 8 == 0 && kAgTile % 8 == 0 && kAgTileSmall % 8 == 0 &&
+                  kRsTileSmall % 8 == 0,
+              "tiles must keep the 16-byte phase");
+static_assert(kAgTileSmall * 4 < (int64_t(1) << 31), "all-gather tile bytes must fit in int");
+constexpr int kBlock = 256;           // lanes per workgroup (4 wave64)
+
+// Per-parameter geometry as the kernels read it.  src(r) = r*seg and
+// L(r) = min(seg, max(0, numel - r*seg)) follow from seg and numel.
+struct ParamDesc {
+    int64_t off;     // offset of the parameter's segment in a rank block
+    int64_t seg;     // c * inner: elements per rank block (padding included)
+    int64_t numel;   // dim0 * inner: elements of the full tensor
+    int64_t span;    // seg plus the alignment gap up to the next offset (or S)
+};
+
+// One tile: `param`'s elements [k0, k0 + tile) of rank `rank`'s segment
+// (all-gather) or of the parameter's span in the block (reduce-scatter,
+// where `rank` is unused: the rank is a launch argument).
+struct Tile {
+    int32_t param;
+    int32_t rank;
+    int64_t k0;
+};
+
+// Kernel shapes (defaults are the measured best on MI355X).
+#ifndef TIDE_RS_CPL
+#define TIDE_RS_CPL 4
+#endif
+#ifndef TIDE_SMALL_BLOCK
+#define TIDE_SMALL_BLOCK 256
+#endif
+#ifndef TIDE_SMALL_PACE
+#define TIDE_SMALL_PACE 0
+#endif
+#ifndef TIDE_RS_RB
+#define TIDE_RS_RB 8
+#endif
+#ifndef TIDE_SMALL_CPL
+#define TIDE_SMALL_CPL 2
+#endif
+#ifndef TIDE_SMALL_RB
+#define TIDE_SMALL_RB 16
+#endif
+#ifndef TIDE_XMAP_RS
+#define TIDE_XMAP_RS 0
+#endif
+#ifndef TIDE_SMALL_AG_U
+#define TIDE_SMALL_AG_U 8
+#endif
+#ifndef TIDE_XMAP_AG
+#define TIDE_XMAP_AG 1
+#endif
+#ifndef TIDE_AG_U
+#define TIDE_AG_U 1
+#endif
+
+constexpr int kRsChunksPerLane = TIDE_RS_CPL;
+constexpr int kAgVecsPerLane = TIDE_AG_U;
+// Spare (null) entries after the reduce-scatter pointer table: a batch of RB
+// ranks loads its RB pointers unconditionally.
+constexpr size_t kPtrPad = 32;
+static_assert(TIDE_RS_RB <= static_cast<int>(kPtrPad) && TIDE_SMALL_RB <= static_cast<int>(kPtrPad),
+              "rank batch larger than the pointer-table padding");
+
+// Gradient element types.  Each widens exactly to fp32: bf16 is the top
+// half of an fp32 pattern, every fp16 value is an fp32 value, fp32 is kept.
+enum GradType { kBf16 = 0, kF16 = 1, kF32 = 2 };
+
+// Everything one TIDE-RS launch needs.  ptrs is the param-major pointer
+// table (entry i*N + r = rank r's gradient of parameter i) plus kPtrPad
+// null entries.  vec_in: every gradient pointer is 16-byte aligned; vec_out:
+// out is 16-byte aligned.  lds: dynamic LDS each workgroup reserves (never
+// touched; it only caps workgroups per CU).
+struct RsLaunch {
+    const ParamDesc *pd;
+    const Tile *tiles;
+    int64_t ntiles;
+    const char *const *ptrs;
+    int N, R, avg;
+    float *out;
+    int vec_in, vec_out;
+    unsigned grid;
+    int lds;
+    hipStream_t stream;
+};
+
+// Everything one TIDE-AG kernel launch needs.  ptrs: the N rank block
+// pointers, then the P parameter pointers.
+struct AgLaunch {
+    const ParamDesc *pd;
+    const Tile *tiles;
+    int64_t ntiles;
+    const uintptr_t *ptrs;
+    int N, elem_bytes;
+    unsigned grid;
+    int lds;
+    hipStream_t stream;
+};
+
+// Enqueue one launch.  `small` selects the small-footprint tile list's
+// kernel shape (the caller passes that tile list).  Returns the HIP error of
+// the launch (or of allowing its LDS reservation).
+hipError_t launch_rs(const RsLaunch &a, GradType type, bool small);
+hipError_t launch_ag(const AgLaunch &a, bool small);
+
+}  // namespace tide

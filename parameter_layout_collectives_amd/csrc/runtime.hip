@@ -1,0 +1,529 @@
+// Runtime of the TIDE library on the HIP side: per-device tables, the
+// pointer-table cache, the launch policy and the extern "C" entry points
+// tide_rs / tide_ag.  The kernels and their launch functions are in
+// kernels.hip; the host-only plan and argument checks in plan.cpp.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+namespace tide {
+namespace {
+
+// Launch policy (defaults are the measured best on MI355X).
+#ifndef TIDE_DEFAULT_ONE_TILE_PER_WG
+#define TIDE_DEFAULT_ONE_TILE_PER_WG 1
+#endif
+#ifndef TIDE_SMALL_LDS_RESERVE
+#define TIDE_SMALL_LDS_RESERVE 1
+#endif
+#ifndef TIDE_SMALL_WG_PER_CU
+#define TIDE_SMALL_WG_PER_CU 1
+#endif
+#ifndef TIDE_SMALL_PERSISTENT
+#define TIDE_SMALL_PERSISTENT 0
+#endif
+#ifndef TIDE_RS_WG_CAP
+#define TIDE_RS_WG_CAP 2
+#endif
+#ifndef TIDE_AG_WG_CAP
+#define TIDE_AG_WG_CAP 0
+#endif
+#ifndef TIDE_WG_PER_CU
+#define TIDE_WG_PER_CU 8
+#endif
+#ifndef TIDE_SMALL_WG
+#define TIDE_SMALL_WG 32
+#endif
+constexpr int kWgPerCu = TIDE_WG_PER_CU;      // default grid: enough waves to keep HBM busy
+constexpr int kSmallFootprintWg = TIDE_SMALL_WG;  // small-footprint grid
+
+tide_status hip_fail(const char *what, hipError_t e) {
+    return fail(TIDE_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+tide_status upload(const void *host, size_t bytes, void **dev, const char *what) {
+    *dev = nullptr;
+    if (bytes == 0) return TIDE_OK;
+    hipError_t e = hipMalloc(dev, bytes);
+    if (e != hipSuccess) {
+        *dev = nullptr;
+        if (e == hipErrorOutOfMemory) return fail(TIDE_E_NOMEM, std::string(what) + ": hipMalloc");
+        return hip_fail(what, e);
+    }
+    e = hipMemcpy(*dev, host, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(*dev);
+        *dev = nullptr;
+        return hip_fail(what, e);
+    }
+    return TIDE_OK;
+}
+
+void free_state(DeviceState *ds) {
+    (void)hipFree(ds->d_params);
+    (void)hipFree(ds->d_rs_tiles);
+    (void)hipFree(ds->d_ag_tiles);
+    (void)hipFree(ds->d_ag_tiles_small);
+    (void)hipFree(ds->d_rs_tiles_small);
+    for (auto *cache : {&ds->rs_cache, &ds->ag_cache})
+        for (auto &pt : *cache) {
+            (void)hipFree(pt.dev);
+            (void)hipHostFree(pt.staging);
+            if (pt.done) (void)hipEventDestroy(static_cast<hipEvent_t>(pt.done));
+            if (pt.uploaded) (void)hipEventDestroy(static_cast<hipEvent_t>(pt.uploaded));
+        }
+    delete ds;
+}
+
+// LDS that lets exactly `cap` workgroups share a CU (0: no cap).
+int lds_for_cap(const DeviceState *ds, int cap) {
+    if (cap <= 0 || ds->lds_per_cu <= 0) return 0;
+    const int want = ds->lds_per_cu / cap - 1024;
+    return (want > 0 && want <= ds->lds_per_wg_max) ? want : 0;
+}
+
+// The plan's tables on the current device (created on first use).
+// Caller holds p->mu.
+tide_status device_state(const tide_plan *p, DeviceState **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    for (DeviceState *ds : p->devs)
+        if (ds->device == dev) {
+            *out = ds;
+            return TIDE_OK;
+        }
+    DeviceState *ds = new (std::nothrow) DeviceState;
+    if (!ds) return fail(TIDE_E_NOMEM, "device state: out of host memory");
+    ds->device = dev;
+    e = hipDeviceGetAttribute(&ds->cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&ds->lds_per_cu,
+                                  hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&ds->lds_per_wg_max, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                                  dev);
+    if (e != hipSuccess) {
+        delete ds;
+        return hip_fail("hipDeviceGetAttribute", e);
+    }
+    // A small-footprint workgroup reserves just over half of a CU's LDS, so
+    // no two of them share a CU: the hardware dispatcher has to spread them
+    // one per CU, and a CU that holds one cannot take two workgroups of an
+    // LDS-heavy kernel running beside it.  The reservation is never touched.
+    ds->small_lds = 0;
+    if (TIDE_SMALL_LDS_RESERVE && ds->lds_per_cu > 0) {
+        const int want = ds->lds_per_cu / 2 + 1024;
+        if (want <= ds->lds_per_wg_max) ds->small_lds = want;
+    }
+    // Optional cap on default reduce-scatter workgroups per CU (same trick:
+    // an untouched LDS reservation of which exactly TIDE_RS_WG_CAP fit).
+    ds->rs_cap_lds = lds_for_cap(ds, TIDE_RS_WG_CAP);
+    ds->ag_cap_lds = lds_for_cap(ds, TIDE_AG_WG_CAP);
+    tide_status st = upload(p->desc.data(), p->desc.size() * sizeof(ParamDesc), &ds->d_params,
+                            "parameter table");
+    if (st == TIDE_OK)
+        st = upload(p->rs_tiles.data(), p->rs_tiles.size() * sizeof(Tile), &ds->d_rs_tiles,
+                    "reduce-scatter tiles");
+    if (st == TIDE_OK)
+        st = upload(p->rs_tiles_small.data(), p->rs_tiles_small.size() * sizeof(Tile),
+                    &ds->d_rs_tiles_small, "reduce-scatter tiles (small footprint)");
+    if (st == TIDE_OK)
+        st = upload(p->ag_tiles.data(), p->ag_tiles.size() * sizeof(Tile), &ds->d_ag_tiles,
+                    "all-gather tiles");
+    if (st == TIDE_OK)
+        st = upload(p->ag_tiles_small.data(), p->ag_tiles_small.size() * sizeof(Tile),
+                    &ds->d_ag_tiles_small, "all-gather tiles (small footprint)");
+    if (st != TIDE_OK) {
+        free_state(ds);
+        return st;
+    }
+    try {
+        p->devs.push_back(ds);
+    } catch (const std::bad_alloc &) {
+        free_state(ds);
+        return fail(TIDE_E_NOMEM, "device state: out of host memory");
+    }
+    *out = ds;
+    return TIDE_OK;
+}
+
+uint64_t hash_ptrs(uint64_t h, const uintptr_t *v, size_t n) {
+    for (size_t i = 0; i < n; i++) {
+        h ^= static_cast<uint64_t>(v[i]);
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+// A pointer set as the caller passed it: `na` entries at `a`, then `nb` at
+// `b` (read in place; copied only when a new table is made).
+struct PtrKey {
+    const uintptr_t *a;
+    size_t na;
+    const uintptr_t *b;
+    size_t nb;
+    size_t size() const { return na + nb; }
+    bool equals(const std::vector<uintptr_t> &k) const {
+        return k.size() == size() && std::memcmp(k.data(), a, na * sizeof(uintptr_t)) == 0 &&
+               (nb == 0 || std::memcmp(k.data() + na, b, nb * sizeof(uintptr_t)) == 0);
+    }
+};
+
+// Records that work on `stream` reads the slot: called after its upload
+// and after every launch that reads it.
+tide_status mark_read(PtrTable *pt, hipStream_t stream) {
+    if (pt->recorded && pt->last_stream != static_cast<void *>(stream)) pt->many_streams = true;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pt->done), stream);
+    if (e != hipSuccess) {
+        // The event no longer covers every reader: reuse waits for the device.
+        pt->recorded = pt->many_streams = true;
+        return hip_fail("pointer table: hipEventRecord", e);
+    }
+    pt->recorded = true;
+    pt->last_stream = static_cast<void *>(stream);
+    return TIDE_OK;
+}
+
+// A launch on `stream` that reads the slot must not start before the upload
+// (enqueued on another stream, perhaps) has finished.
+tide_status order_after_upload(PtrTable *pt, hipStream_t stream) {
+    if (pt->upload_done || pt->upload_stream == static_cast<void *>(stream)) return TIDE_OK;
+    const hipEvent_t up = static_cast<hipEvent_t>(pt->uploaded);
+    hipError_t e = hipEventQuery(up);
+    if (e == hipSuccess) {
+        pt->upload_done = true;
+        return TIDE_OK;
+    }
+    if (e != hipErrorNotReady) return hip_fail("pointer table: hipEventQuery", e);
+    e = hipStreamWaitEvent(stream, up, 0);
+    if (e != hipSuccess) return hip_fail("pointer table: hipStreamWaitEvent", e);
+    return TIDE_OK;
+}
+
+// Allocates a slot's device table, pinned staging buffer and events.
+tide_status new_slot(size_t bytes, PtrTable *pt) {
+    hipError_t e = hipMalloc(&pt->dev, bytes);
+    if (e == hipSuccess) e = hipHostMalloc(&pt->staging, bytes, hipHostMallocDefault);
+    hipEvent_t ev = nullptr, up = nullptr;
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&up, hipEventDisableTiming);
+    pt->done = ev;
+    pt->uploaded = up;
+    if (e == hipSuccess) return TIDE_OK;
+    (void)hipFree(pt->dev);
+    (void)hipHostFree(pt->staging);
+    if (ev) (void)hipEventDestroy(ev);
+    if (up) (void)hipEventDestroy(up);
+    pt->dev = pt->staging = pt->done = pt->uploaded = nullptr;
+    if (e == hipErrorOutOfMemory) return fail(TIDE_E_NOMEM, "pointer table: allocation");
+    return hip_fail("pointer table: allocation", e);
+}
+
+// Waits until no launch can still read the slot's device table (and so no
+// upload can still read its staging buffer).  A slot read on one stream
+// waits for its event; one read on several streams waits for the device.
+tide_status drain_slot(PtrTable *pt) {
+    if (!pt->recorded) return TIDE_OK;
+    hipError_t e = pt->many_streams ? hipDeviceSynchronize()
+                                    : hipEventSynchronize(static_cast<hipEvent_t>(pt->done));
+    if (e != hipSuccess) return hip_fail("pointer table: waiting for its last reader", e);
+    return TIDE_OK;
+}
+
+// Finds the slot that holds a pointer set, or fills one with it.  A hit
+// costs one hash and one compare over the caller's arrays.  On a miss a
+// free slot is taken (at most kPtrCacheEntries per cache), else the least
+// recently used one once its last reader has finished; `order(key, dev)`
+// writes the array as the kernel wants it (`dev_len` entries: a permutation
+// of the key, possibly padded) into the slot's pinned staging buffer, and an
+// async copy on `stream` uploads it.  After launching, the caller must call
+// mark_read().  Caller holds p->mu.
+template <typename Order>
+tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const PtrKey &key,
+                          size_t dev_len, Order order, hipStream_t stream, PtrTable **out) {
+    const uint64_t h = hash_ptrs(hash_ptrs(1469598103934665603ull, key.a, key.na), key.b, key.nb);
+    for (auto &pt : cache)
+        if (pt.hash == h && key.equals(pt.key)) {
+            tide_status st = order_after_upload(&pt, stream);
+            if (st != TIDE_OK) return st;
+            pt.last_use = ++ds->tick;
+            *out = &pt;
+            return TIDE_OK;
+        }
+    const size_t bytes = dev_len * sizeof(uintptr_t);
+    PtrTable *pt = nullptr;
+    if (cache.size() < kPtrCacheEntries) {
+        PtrTable fresh;
+        tide_status st = new_slot(bytes, &fresh);
+        if (st != TIDE_OK) return st;
+        try {
+            cache.reserve(kPtrCacheEntries);
+            cache.push_back(std::move(fresh));
+        } catch (const std::bad_alloc &) {
+            (void)hipFree(fresh.dev);
+            (void)hipHostFree(fresh.staging);
+            (void)hipEventDestroy(static_cast<hipEvent_t>(fresh.done));
+            (void)hipEventDestroy(static_cast<hipEvent_t>(fresh.uploaded));
+            return fail(TIDE_E_NOMEM, "pointer table: out of host memory");
+        }
+        pt = &cache.back();
+    } else {
+        pt = &*std::min_element(cache.begin(), cache.end(),
+                                [](const PtrTable &a, const PtrTable &b) {
+                                    return a.last_use < b.last_use;
+                                });
+        tide_status drained = drain_slot(pt);
+        if (drained != TIDE_OK) return drained;
+    }
+    // The slot holds no valid set until the upload is enqueued.
+    pt->hash = 0;
+    pt->key.clear();
+    pt->recorded = pt->many_streams = false;
+    try {
+        pt->key.resize(key.size());
+    } catch (const std::bad_alloc &) {
+        return fail(TIDE_E_NOMEM, "pointer table: out of host memory");
+    }
+    std::copy(key.a, key.a + key.na, pt->key.begin());
+    if (key.nb) std::copy(key.b, key.b + key.nb, pt->key.begin() + key.na);
+    uintptr_t *staged = static_cast<uintptr_t *>(pt->staging);
+    std::fill(staged, staged + dev_len, uintptr_t{0});
+    order(pt->key.data(), staged);
+    hipError_t e = hipMemcpyAsync(pt->dev, staged, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) {
+        pt->key.clear();
+        return hip_fail("pointer table: upload", e);
+    }
+    // The copy reads the staging buffer: the slot is not reusable before it
+    // ends, and launches on other streams wait for it.
+    tide_status st = mark_read(pt, stream);
+    if (st == TIDE_OK) {
+        e = hipEventRecord(static_cast<hipEvent_t>(pt->uploaded), stream);
+        if (e != hipSuccess) st = hip_fail("pointer table: hipEventRecord", e);
+    }
+    if (st != TIDE_OK) {
+        pt->key.clear();
+        return st;
+    }
+    pt->upload_stream = static_cast<void *>(stream);
+    pt->upload_done = false;
+    pt->hash = h;
+    pt->aligned16 = true;
+    for (uintptr_t a : pt->key) pt->aligned16 = pt->aligned16 && (a & 15) == 0;
+    pt->last_use = ++ds->tick;
+    *out = pt;
+    return TIDE_OK;
+}
+
+// Both launch modes give every tile its own short-lived workgroup, and the
+// hardware dispatcher balances them over all CUs.  Small-footprint launches
+// also reserve over half a CU's LDS per workgroup, so at most one of them
+// is resident on a CU at any moment: a concurrent GEMM keeps its place on
+// every CU and loses only a little issue bandwidth there.  max_wg > 0 caps
+// the grid (workgroups then loop over tiles).
+unsigned grid_size(const DeviceState *ds, int64_t ntiles, uint32_t flags, int32_t max_wg) {
+    int64_t g;
+    if (flags & TIDE_F_SMALL_FOOTPRINT)
+        g = !TIDE_SMALL_PERSISTENT ? ntiles
+            : ds->small_lds        ? static_cast<int64_t>(ds->cus) * TIDE_SMALL_WG_PER_CU
+                                   : kSmallFootprintWg;
+    else if (TIDE_DEFAULT_ONE_TILE_PER_WG)
+        g = ntiles;
+    else
+        g = static_cast<int64_t>(ds->cus) * kWgPerCu;
+    if (max_wg > 0) g = max_wg;
+    g = std::min<int64_t>({g, ntiles, 0x7fffffff});
+    return static_cast<unsigned>(std::max<int64_t>(g, 1));
+}
+
+}  // namespace
+
+void release_device_states(const tide_plan *p) {
+    std::lock_guard<std::mutex> lock(p->mu);
+    int cur = -1;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (DeviceState *ds : p->devs) {
+        if (hipSetDevice(ds->device) == hipSuccess) (void)hipDeviceSynchronize();
+        free_state(ds);
+    }
+    p->devs.clear();
+    if (have_cur) (void)hipSetDevice(cur);
+}
+
+}  // namespace tide
+
+using tide::fail;
+
+extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *const *grads,
+                               float *out, uint32_t flags, int32_t max_workgroups,
+                               void *stream) {
+    tide_status st = tide::check_rs_args(plan, rank, grads, out, flags, max_workgroups);
+    if (st != TIDE_OK) return st;
+    if (plan->S == 0) return TIDE_OK;
+
+    // The kernel reads the table parameter-major (entry i*N + r), followed by
+    // kPtrPad null entries so that a batch's pointers load in one scalar load.
+    const int32_t N = plan->N, P = plan->P;
+    const tide::PtrKey key{reinterpret_cast<const uintptr_t *>(grads),
+                           static_cast<size_t>(N) * P, nullptr, 0};
+    auto param_major = [N, P](const uintptr_t *k, uintptr_t *dev) {
+        for (int32_t r = 0; r < N; r++)
+            for (int32_t i = 0; i < P; i++)
+                dev[static_cast<size_t>(i) * N + r] = k[static_cast<size_t>(r) * P + i];
+    };
+
+    std::lock_guard<std::mutex> lock(plan->mu);
+    tide::DeviceState *ds = nullptr;
+    st = tide::device_state(plan, &ds);
+    if (st != TIDE_OK) return st;
+    tide::PtrTable *pt = nullptr;
+    st = tide::pointer_table(ds, ds->rs_cache, key, key.size() + tide::kPtrPad, param_major,
+                             static_cast<hipStream_t>(stream), &pt);
+    if (st != TIDE_OK) return st;
+
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    const int64_t ntiles =
+        static_cast<int64_t>(small ? plan->rs_tiles_small.size() : plan->rs_tiles.size());
+    const tide::RsLaunch L{static_cast<const tide::ParamDesc *>(ds->d_params),
+                           static_cast<const tide::Tile *>(small ? ds->d_rs_tiles_small
+                                                                 : ds->d_rs_tiles),
+                           ntiles,
+                           static_cast<const char *const *>(pt->dev),
+                           plan->N,
+                           rank,
+                           (flags & TIDE_F_AVG) ? 1 : 0,
+                           out,
+                           pt->aligned16 ? 1 : 0,
+                           (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
+                           tide::grid_size(ds, ntiles, flags, max_workgroups),
+                           small ? ds->small_lds : ds->rs_cap_lds,
+                           static_cast<hipStream_t>(stream)};
+    const tide::GradType type = (flags & TIDE_F_GRAD_F32)   ? tide::kF32
+                                : (flags & TIDE_F_GRAD_F16) ? tide::kF16
+                                                            : tide::kBf16;
+    hipError_t e = tide::launch_rs(L, type, small);
+    if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
+    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    if (st != TIDE_OK) return st;
+    tide::clear_error();
+    return TIDE_OK;
+}
+
+namespace tide {
+namespace {
+
+// TIDE-AG placement with the SDMA engines: the same (parameter, rank) runs as
+// the kernel copies, as device-to-device copies that use no compute unit.
+// The ranks holding a full shard of parameter i form a prefix 0..F-1; when
+// the rank blocks are equally spaced (one gathered buffer) those F runs are
+// one 2-D copy: F rows of seg_i elements, source pitch = block spacing,
+// destination pitch = seg_i.  The one short rank (if any) is a 1-D copy.
+tide_status ag_copy_engine(const tide_plan *p, const void *const *rank_src, void *const *params,
+                           int32_t e, hipStream_t stream) {
+    const hipMemcpyKind kind = hipMemcpyDeviceToDeviceNoCU;
+    const uintptr_t eb = static_cast<uintptr_t>(e);
+    bool equal = p->N > 1;
+    uintptr_t pitch = 0;
+    if (equal) {
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(rank_src[0]);
+        const uintptr_t b1 = reinterpret_cast<uintptr_t>(rank_src[1]);
+        equal = b1 > b0;
+        pitch = b1 - b0;
+        for (int32_t r = 2; equal && r < p->N; r++)
+            equal = reinterpret_cast<uintptr_t>(rank_src[r]) ==
+                    reinterpret_cast<uintptr_t>(rank_src[r - 1]) + pitch;
+    }
+    for (int32_t i = 0; i < p->P; i++) {
+        if (p->numel[i] == 0 || p->seg[i] == 0) continue;
+        const uintptr_t seg_b = static_cast<uintptr_t>(p->seg[i]) * eb;
+        const uintptr_t off_b = static_cast<uintptr_t>(p->off[i]) * eb;
+        char *dst = static_cast<char *>(params[i]);
+        int32_t full = 0;
+        while (full < p->N) {
+            int64_t src, L;
+            shard_run(p, full, i, &src, &L);
+            if (L != p->seg[i]) break;
+            full++;
+        }
+        hipError_t err = hipSuccess;
+        if (equal && full > 1 && pitch >= seg_b) {
+            err = hipMemcpy2DAsync(dst, seg_b, static_cast<const char *>(rank_src[0]) + off_b,
+                                   pitch, seg_b, static_cast<size_t>(full), kind, stream);
+        } else {
+            for (int32_t r = 0; r < full && err == hipSuccess; r++)
+                err = hipMemcpyAsync(dst + static_cast<uintptr_t>(r) * seg_b,
+                                     static_cast<const char *>(rank_src[r]) + off_b, seg_b, kind,
+                                     stream);
+        }
+        if (err == hipSuccess && full < p->N) {
+            int64_t src, L;
+            shard_run(p, full, i, &src, &L);
+            if (L > 0)
+                err = hipMemcpyAsync(dst + static_cast<uintptr_t>(src) * eb,
+                                     static_cast<const char *>(rank_src[full]) + off_b,
+                                     static_cast<uintptr_t>(L) * eb, kind, stream);
+        }
+        if (err != hipSuccess) return hip_fail("tide_ag: copy-engine copy", err);
+    }
+    return TIDE_OK;
+}
+
+}  // namespace
+}  // namespace tide
+
+extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_src,
+                               void *const *params, int32_t elem_bytes, uint32_t flags,
+                               int32_t max_workgroups, void *stream) {
+    tide_status st =
+        tide::check_ag_args(plan, rank_src, params, elem_bytes, flags, max_workgroups);
+    if (st != TIDE_OK) return st;
+    if (plan->ag_tiles.empty()) return TIDE_OK;
+    if (flags & TIDE_F_COPY_ENGINE) {
+        st = tide::ag_copy_engine(plan, rank_src, params, elem_bytes,
+                                  static_cast<hipStream_t>(stream));
+        if (st == TIDE_OK) tide::clear_error();
+        return st;
+    }
+
+    // Table: the N rank block pointers, then the P parameter pointers.
+    const tide::PtrKey key{reinterpret_cast<const uintptr_t *>(rank_src),
+                           static_cast<size_t>(plan->N),
+                           reinterpret_cast<const uintptr_t *>(params),
+                           static_cast<size_t>(plan->P)};
+    const size_t n = key.size();
+    auto as_is = [n](const uintptr_t *k, uintptr_t *dev) { std::copy(k, k + n, dev); };
+
+    std::lock_guard<std::mutex> lock(plan->mu);
+    tide::DeviceState *ds = nullptr;
+    st = tide::device_state(plan, &ds);
+    if (st != TIDE_OK) return st;
+    tide::PtrTable *pt = nullptr;
+    st = tide::pointer_table(ds, ds->ag_cache, key, n, as_is, static_cast<hipStream_t>(stream),
+                             &pt);
+    if (st != TIDE_OK) return st;
+
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    const int64_t ntiles =
+        static_cast<int64_t>(small ? plan->ag_tiles_small.size() : plan->ag_tiles.size());
+    const tide::AgLaunch L{static_cast<const tide::ParamDesc *>(ds->d_params),
+                           static_cast<const tide::Tile *>(small ? ds->d_ag_tiles_small
+                                                                 : ds->d_ag_tiles),
+                           ntiles,
+                           static_cast<const uintptr_t *>(pt->dev),
+                           plan->N,
+                           elem_bytes,
+                           tide::grid_size(ds, ntiles, flags, max_workgroups),
+                           small ? ds->small_lds : ds->ag_cap_lds,
+                           static_cast<hipStream_t>(stream)};
+    hipError_t e = tide::launch_ag(L, small);
+    if (e != hipSuccess) return tide::hip_fail("tide_ag: kernel launch", e);
+    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    if (st != TIDE_OK) return st;
+    tide::clear_error();
+    return TIDE_OK;
+}

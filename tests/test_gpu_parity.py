@@ -483,3 +483,32 @@ def test_concurrent_calls_on_one_plan(orc):
     for t in range(8):
         want = expected_rs(orc, shapes, N, t % N, g, plan)
         assert same_f32(outs[t].cpu().numpy(), want), t
+
+
+def test_table_upload_ordered_across_streams(orc):
+    """A new pointer set is uploaded by an async copy on the caller's stream.
+    Here that stream is held back by a spin kernel; a second call with the
+    same set on another stream must wait for the upload.  Every slot first
+    holds a valid set, so reading the slot too early would give another
+    set's sums, not a fault."""
+    shapes = [(37, 5), (4100,)]
+    N = 3
+    plan = tide.Plan(shapes, N)
+    sets = [to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=2000 + 10 * j))
+            for j in range(9)]
+    scratch = fresh_out(plan.S)
+    for j in range(8):                       # fill the 8 slots of the cache
+        run_rs(plan, 0, sets[j], scratch)
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    out_a, out_b = fresh_out(plan.S), fresh_out(plan.S)
+    torch.cuda.synchronize()
+    note("upload on a held-back stream, hit on another stream")
+    with torch.cuda.stream(a):
+        torch.cuda._sleep(20_000_000)        # bounded spin: holds stream a back
+    tide.rs(plan, 1, sets[8], out_a, stream=a)   # replaces slot of set 0; upload queued on a
+    tide.rs(plan, 1, sets[8], out_b, stream=b)   # hit: must wait for that upload
+    torch.cuda.synchronize()
+    want = expected_rs(orc, shapes, N, 1, sets[8], plan)
+    for out in (out_a, out_b):
+        got = out.cpu().numpy()
+        assert same_f32(got, want), first_mismatch(got, want)
