@@ -15,6 +15,9 @@ What it computes (cited by page title and section):
     analysis" §"分片中的通信原语").
   * ``rs_traffic``: elements pulled from peers, (N-1)/N*Psi per rank on
     average (apxml "Communication volume analysis" §"带宽饱和和节点扩展").
+  * ``round_bf16``: fp32 -> bf16, round to nearest, ties to even; a bf16
+    shard is the fp32 block from ``rs`` rounded once (the reduction itself
+    stays fp32: tqpw.cn blog §3.2, TIDE article §"TIDE的设计思路").
 
 Arrays of bf16 values are carried as numpy ``uint16`` bit patterns.
 """
@@ -98,9 +101,11 @@ class Oracle:
         lib.oracle_ag.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
         lib.oracle_rs_traffic.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_round_bf16.argtypes = [_p, _p, _i64]
         for fn in (lib.oracle_geometry, lib.oracle_shard_run, lib.oracle_rs,
                    lib.oracle_rs_slices, lib.oracle_rs_typed, lib.oracle_rs_slices_typed,
-                   lib.oracle_ag, lib.oracle_rs_traffic, lib.oracle_threads):
+                   lib.oracle_ag, lib.oracle_rs_traffic, lib.oracle_threads,
+                   lib.oracle_round_bf16):
             fn.restype = ctypes.c_int
         lib.oracle_set_threads.restype = None
         self.lib = lib
@@ -172,6 +177,18 @@ class Oracle:
                                       out.ctypes.data)
         if rc != 0:
             raise ValueError("oracle_rs_typed: invalid arguments")
+        return out
+
+    def round_bf16(self, x):
+        """fp32 values (float32 array, or uint32 bit patterns) -> uint16 bf16
+        bit patterns, each rounded to nearest with ties to even."""
+        x = np.asarray(x)
+        if x.dtype == np.uint32:
+            x = x.view(np.float32)
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, np.uint16)
+        if self.lib.oracle_round_bf16(x.ctypes.data, out.ctypes.data, x.size) != 0:
+            raise ValueError("oracle_round_bf16: invalid arguments")
         return out
 
     def rs_slices(self, shapes, N, R, slices, align=1, dtype="bf16", avg=False):

@@ -41,13 +41,17 @@
  *   - the mean (when asked for) is the rank-order sum divided by N with one
  *     correctly rounded binary32 division (the volume page describes the
  *     reduce-scatter of gradients as averaging; the TIDE article as a
- *     reduction to fp32; the sum is the default contract).
+ *     reduction to fp32; the sum is the default contract);
+ *   - a bf16 shard (when asked for) is the fp32 result above rounded once
+ *     to bf16, to nearest with ties to even (the reduction itself stays in
+ *     fp32, as the blog's reduction dtype and the TIDE article require).
  *
  * Build: gcc -std=c11 -O2 -fno-fast-math -ffp-contract=off -fopenmp
  *        (see oracle/build_oracle.py).  OpenMP splits independent output
  *        elements only; the per-element rank loop is always sequential, so the
  *        thread count never changes a bit.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -274,6 +278,49 @@ int oracle_rs_slices(int32_t N, int32_t P, const int64_t *d0, const int64_t *inn
                      int64_t align, int32_t R, const uint16_t *const *slices, float *out)
 {
     return rs_body(N, P, d0, inner, align, R, ORACLE_BF16, 0, (const void *const *)slices, out);
+}
+
+/* ---------------------------------------------------------------------- */
+/* fp32 -> bf16 rounding of a reduced shard.                               */
+/* ---------------------------------------------------------------------- */
+
+/* The value of a bf16 pattern, as a double (exact). */
+static double bf16_value(uint16_t b) { return (double)widen_bf16(b); }
+
+/* x rounded to bf16: IEEE round to nearest, ties to even.
+ * A bf16 keeps an fp32's sign, 8-bit exponent and top 7 fraction bits, so
+ * the bf16 values around a finite x are t, x's pattern with its low 16 bits
+ * cleared (x cut toward zero), and t + 1 as a pattern, the next bf16 away
+ * from zero (sign-magnitude patterns grow with magnitude).  x goes to the
+ * nearer of the two, and on a tie to the one whose last bit is 0.  Above
+ * the largest finite bf16 the upper neighbour is infinity, whose distance
+ * is measured as if it were 2^128 (IEEE's rule for overflow).  All
+ * distances are exact in double.  Zeros and infinities are kept; a NaN stays
+ * a NaN (its quiet bit set, so that cutting the payload cannot give an
+ * infinity). */
+static uint16_t round_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040u);
+    uint16_t t = (uint16_t)(u >> 16);
+    if ((u & 0xffffu) == 0) return t;          /* representable (zeros, infinities too) */
+    uint16_t up = (uint16_t)(t + 1u);
+    double ax = fabs((double)x);
+    double at = fabs(bf16_value(t));
+    double aup = ((up & 0x7fffu) == 0x7f80u) ? ldexp(1.0, 128) : fabs(bf16_value(up));
+    double d_t = ax - at, d_up = aup - ax;
+    if (d_t < d_up) return t;
+    if (d_up < d_t) return up;
+    return (t & 1u) ? up : t;
+}
+
+/* out[k] = round_bf16(in[k]) for k < n. */
+int oracle_round_bf16(const float *in, uint16_t *out, int64_t n)
+{
+    if (n < 0 || (n > 0 && (!in || !out))) return ORACLE_EINVAL;
+    for (int64_t k = 0; k < n; k++) out[k] = round_bf16(in[k]);
+    return ORACLE_OK;
 }
 
 /* ---------------------------------------------------------------------- */

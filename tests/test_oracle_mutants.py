@@ -57,6 +57,12 @@ MUTANTS = {
     "f16_subnormal_scale": ("f = (float)frac * 0x1p-24f;", "f = (float)frac * 0x1p-25f;"),
     "f16_nan_drops_payload": ("bits = (sign << 31) | 0x7f800000u | (frac << 13);",
                               "bits = (sign << 31) | 0x7f800000u | (frac ? 0x400000u : 0u);"),
+    "round_ties_away_from_zero": ("return (t & 1u) ? up : t;", "return up;"),
+    "round_toward_zero": ("    if (d_up < d_t) return up;\n", ""),
+    "round_nan_payload_cut": ("if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040u);",
+                              "if (isnan(x)) return (uint16_t)(u >> 16);"),
+    "round_overflow_saturates": ("double aup = ((up & 0x7fffu) == 0x7f80u) ? ldexp(1.0, 128)",
+                                 "if ((up & 0x7fffu) == 0x7f80u) return t;\n    double aup = 0 ? 0"),
     "f32_read_as_half_width": ("memcpy(&f, (const char *)run + 4 * k, sizeof f);",
                                "memcpy(&f, (const char *)run + 2 * k, sizeof f);"),
 }

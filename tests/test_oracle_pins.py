@@ -21,7 +21,11 @@ Pins used (none of them re-types the oracle's formulas):
   * gradient element types and the mean: every binary16 pattern widened as
     numpy does, N=2 and integer-valued sums of fp16/fp32 gradients, the mean
     as an exact power-of-two scaling (N = 2^k) or as the exact rational
-    sum/N rounded to nearest even (other N).
+    sum/N rounded to nearest even (other N);
+  * fp32 -> bf16 rounding of a shard: torch's own conversion over millions
+    of patterns (every low half under chosen high halves), a search over all
+    65,536 bf16 values for the nearest one, worked ties, and an N=2 shard
+    equal to torch's (a + b) in fp32 converted to bf16.
 """
 import json
 import os
@@ -393,6 +397,102 @@ def pin_mean_exact_rounding(orc):
                 want = brute.round_f32(Fraction(float(s_[k])) / N)
                 assert bits_f32([m[k]])[0] == bits_f32([want])[0], (N, R, k)
             assert np.all(bits_f32(m[L:g.seg[0]]) == 0)          # padding stays +0
+
+
+# --------------------------------------------------------------------------
+# fp32 -> bf16 rounding of a shard
+# --------------------------------------------------------------------------
+
+def _torch_bf16_bits(x_f32):
+    return torch.from_numpy(np.ascontiguousarray(x_f32, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def _check_rounding(orc, pats):
+    """Oracle vs torch's fp32 -> bf16 conversion (round to nearest even):
+    bitwise for non-NaN inputs; NaN inputs must give a NaN."""
+    x = np.ascontiguousarray(pats, np.uint32).view(np.float32)
+    got = orc.round_bf16(x)
+    want = _torch_bf16_bits(x)
+    nan = np.isnan(x)
+    bad = np.nonzero((got != want) & ~nan)[0]
+    assert bad.size == 0, [(hex(int(pats[k])), hex(int(got[k])), hex(int(want[k]))) for k in bad[:5]]
+    got_f = (got[nan].astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(got_f))
+
+
+def pin_round_bf16_library(orc):
+    rng = np.random.default_rng(404)
+    _check_rounding(orc, rng.integers(0, 2 ** 32, size=1 << 21, dtype=np.uint64).astype(np.uint32))
+    low = np.arange(1 << 16, dtype=np.uint32)
+    # every low half under: zero/subnormal, smallest normal, 1.0, largest
+    # finite (overflow to inf), their negatives, and an infinity (NaNs).
+    for hi in (0x0000, 0x0001, 0x0080, 0x3F80, 0x3F81, 0x7F7F, 0x7F80, 0x8000, 0xBF80, 0xFF7F,
+               0xFF80):
+        _check_rounding(orc, (np.uint32(hi) << 16) | low)
+
+
+def _nearest_bf16_by_search(x):
+    """The bf16 nearest to the finite float32 x, ties to the even pattern,
+    by comparing x with every finite bf16 value and both infinities
+    (counted as +-2^128 for the distance).  float64 distances are exact for
+    the two nearest candidates."""
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    keep = ((pats & 0x7F80) != 0x7F80) | ((pats & 0x7F) == 0)     # drop the NaNs
+    pats = pats[keep]
+    vals = (pats << 16).view(np.float32).astype(np.float64)
+    vals = np.where(np.isinf(vals), np.sign(vals) * 2.0 ** 128, vals)
+    d = np.abs(vals - float(x))
+    best = np.nonzero(d == d.min())[0]
+    cands = [int(pats[b]) for b in best]
+    if len(cands) > 1:
+        nonzero = [c for c in cands if c & 0x7FFF]
+        if not nonzero:                      # +0 and -0: keep x's sign
+            return 0x8000 if np.signbit(x) else 0
+        cands = [c for c in cands if c % 2 == 0] or cands
+    return cands[0]
+
+
+def pin_round_bf16_global_nearest(orc):
+    rng = np.random.default_rng(405)
+    xs = [rng.standard_normal() * 10.0 ** rng.integers(-40, 39) for _ in range(120)]
+    xs = np.array(xs, np.float32)
+    ties = (rng.integers(0, 1 << 16, size=60).astype(np.uint32) << 16) | 0x8000
+    ties = ties[(ties & 0x7F800000) != 0x7F800000].view(np.float32)
+    xs = np.concatenate([xs, ties, np.array([3.4028235e38, -3.39e38, 1e-45, -1e-41], np.float32)])
+    got = orc.round_bf16(xs)
+    for x, g in zip(xs, got):
+        assert int(g) == _nearest_bf16_by_search(x), (float(x), hex(int(g)))
+
+
+def pin_round_bf16_worked_ties(orc):
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: to the even one, 1.
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: to 1 + 2^-6.
+    # 2^-134 is half the smallest bf16 subnormal 2^-133: to +0.
+    # 3*2^-134 lies between 2^-133 (odd) and 2^-132 (even): to 2^-132.
+    # The largest finite float exceeds the largest bf16 by more than half
+    # a unit of it: to infinity.
+    xs = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 2.0 ** -134, 3 * 2.0 ** -134,
+                   -(1 + 2.0 ** -8), 3.4028235e38], np.float32)
+    want = [0x3F80, 0x3F82, 0x0000, 0x0002, 0xBF80, 0x7F80]
+    assert [int(v) for v in orc.round_bf16(xs)] == want
+
+
+def pin_bf16_shard_n2_is_library_sum(orc):
+    # N = 2: the shard is fl32(g0 + g1) rounded once to bf16, which torch
+    # computes as (a.float() + b.float()).to(bfloat16).
+    shapes = [(37, 5), (64,)]
+    grads = _rand_case(shapes, 2, 77)
+    g = orc.geometry(shapes, 2)
+    for R in (0, 1):
+        got = orc.round_bf16(orc.rs(shapes, 2, R, grads))
+        for i in range(len(shapes)):
+            src, L = g.run(R, i)
+            a = torch.from_numpy(grads[0][i].reshape(-1)[src:src + L].view(np.int16)).view(torch.bfloat16)
+            b = torch.from_numpy(grads[1][i].reshape(-1)[src:src + L].view(np.int16)).view(torch.bfloat16)
+            want = (a.float() + b.float()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(got[g.off[i]:g.off[i] + L], want), (R, i)
+            assert np.all(got[g.off[i] + L:g.off[i] + g.seg[i]] == 0)
 
 
 # --------------------------------------------------------------------------
