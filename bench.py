@@ -156,6 +156,33 @@ class Step:
         return wall, t_rs, t_ag
 
 
+def rs_variants(step, reps=20, warmup=3):
+    """Event-timed tide_rs launches of the flag variants on the step's
+    workload, R rotating: the bf16 shard (fp32 sum rounded once; half the
+    write bytes) and the mean.  Bytes per launch: 2*N*sum_i L(R,i) reads
+    plus S * (4 or 2) writes."""
+    plan, N = step.plan, step.w.world
+    out16 = torch.zeros(N, plan.S, dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for name, out, kw, nbytes in (
+            ("bf16_out", out16, {}, step.b_rs - 2 * plan.S),
+            ("mean", step.blocks, {"avg": True}, step.b_rs)):
+        for k in range(warmup):
+            tide.rs(plan, k % N, step.table, out[k % N], **kw)
+        ev = timed_events(reps)
+        torch.cuda.synchronize()
+        for k in range(reps):
+            ev[k][0].record()
+            tide.rs(plan, k % N, step.table, out[k % N], **kw)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        res[name] = kernel_stats(f"tide_rs ({name})", nbytes, [a.elapsed_time(b) * 1e-3
+                                                              for a, b in ev])
+        log(f"tide_rs {name}: {res[name]['GBps']:.1f} GB/s")
+    del out16
+    return res
+
+
 def kernel_stats(name, nbytes, times):
     mean = statistics.fmean(times)
     q = sorted(times)
@@ -415,6 +442,8 @@ def main():
                     help="workload for the co-run GEMM measurement, or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the tide_rs flag variants (bf16 shard, mean)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -456,6 +485,7 @@ def main():
         "mean_launch_us": dom["mean_us"],
     }
 
+    variants = None if args.no_variants else rs_variants(step)
     copy_gbps = None if args.no_copy else copy_ceiling()
     if copy_gbps:
         log(f"copy ceiling {copy_gbps:.1f} GB/s")
@@ -506,6 +536,7 @@ def main():
         "copy_ceiling_GBps": copy_gbps,
         "tide_rs": rs_k,
         "tide_ag": ag_k,
+        "tide_rs_variants": variants,
         "corun": corun_res,
         "corun_ag": corun_ag_res,
         "gemm_slowdown_pct": None if not corun_res else {

@@ -102,6 +102,13 @@ typedef struct tide_plan tide_plan;
 #define TIDE_F_GRAD_F16 0x8u
 #define TIDE_F_GRAD_F32 0x10u
 
+/* Flag, tide_rs only: write the shard in bf16 - each fp32 result (sum or
+ * mean, computed exactly as without the flag) rounded once to bf16, to
+ * nearest with ties to even (a NaN stays a NaN).  The reduction itself stays
+ * in fp32, the reduction dtype of FSDP mixed precision (tqpw.cn blog §3.2);
+ * only the stored shard is narrowed, halving its bytes. */
+#define TIDE_F_OUT_BF16 0x20u
+
 /* Flag, tide_rs only: write the mean instead of the sum - each rank-order
  * fp32 sum divided by N with one correctly rounded binary32 division
  * (apxml "Communication volume analysis" §"分片中的通信原语" describes the
@@ -146,7 +153,8 @@ tide_status tide_plan_real(const tide_plan *plan, int32_t rank, int32_t i,
 /* §"分片中的通信原语"; fp32 reduction dtype, tqpw.cn blog §3.2).            */
 /* ---------------------------------------------------------------------- */
 
-/* Write rank `rank`'s fp32 block (S floats) of the reduce-scatter:
+/* Write rank `rank`'s block (S elements, fp32 or by flag bf16) of the
+ * reduce-scatter:
  *   out[off_i + k] = sum over r = 0..N-1, in that order, of
  *                    widen(grads[r*P + i][src(rank,i) + k])   for k < L(rank,i)
  *                    (divided by N with TIDE_F_AVG)
@@ -154,6 +162,7 @@ tide_status tide_plan_real(const tide_plan *plan, int32_t rank, int32_t i,
  * widen(b) is exact (bf16 bits shifted into the top of an fp32; fp16 and
  * fp32 convert exactly); every add is one IEEE binary32 round-to-nearest-even
  * addition with subnormals kept, so the result is bit-for-bit reproducible.
+ * With TIDE_F_OUT_BF16 each value above is then rounded once to bf16.
  *   plan    a plan from tide_plan_create.
  *   rank    0 <= rank < N.
  *   grads   host array of N*P device pointers; entry r*P + i is rank r's
@@ -161,17 +170,18 @@ tide_status tide_plan_real(const tide_plan *plan, int32_t rank, int32_t i,
  *           aligned to its element size (bf16 by default, fp16 or fp32 by
  *           flag).  Only the elements of rank `rank`'s shard are read.
  *           Entries with L(rank,i) = 0 may be NULL.
- *   out     device pointer to S floats (4-byte aligned), e.g. block `rank`
- *           of an N*S buffer; must not overlap any element that is read.
- *   flags   any of TIDE_F_SMALL_FOOTPRINT, TIDE_F_AVG and one of
- *           TIDE_F_GRAD_F16 / TIDE_F_GRAD_F32 (both: TIDE_E_INVALID);
+ *   out     device pointer to S floats (4-byte aligned), or with
+ *           TIDE_F_OUT_BF16 to S bf16 values (2-byte aligned), e.g. block
+ *           `rank` of an N*S buffer; must not overlap any element that is read.
+ *   flags   any of TIDE_F_SMALL_FOOTPRINT, TIDE_F_AVG, TIDE_F_OUT_BF16 and
+ *           one of TIDE_F_GRAD_F16 / TIDE_F_GRAD_F32 (both: TIDE_E_INVALID);
  *           TIDE_F_COPY_ENGINE or other bits -> TIDE_E_UNSUPPORTED.
  *   max_workgroups  0 = the policy for `flags`; > 0 caps the grid.
  *   stream  hipStream_t (NULL = null stream).
  * 16-byte aligned pointers take the vector path; other alignments are
  * handled element by element with identical results. */
 tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *const *grads,
-                    float *out, uint32_t flags, int32_t max_workgroups, void *stream);
+                    void *out, uint32_t flags, int32_t max_workgroups, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* TIDE-AG placement (TIDE article §"TIDE的设计思路"; all-gather semantics  */

@@ -22,6 +22,7 @@ COPY_ENGINE = 0x2
 AVG = 0x4
 GRAD_F16 = 0x8
 GRAD_F32 = 0x10
+OUT_BF16 = 0x20
 
 # gradient dtype -> tide_rs flag selecting it
 _GRAD_FLAG = {torch.bfloat16: 0, torch.float16: GRAD_F16, torch.float32: GRAD_F32}
@@ -149,20 +150,23 @@ def _numel(shape):
 
 
 def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=False):
-    """TIDE-RS: write rank `rank`'s fp32 block (plan.S floats) into `out`.
+    """TIDE-RS: write rank `rank`'s block (plan.S elements) into `out`.
 
     grads: list over ranks of lists over params of device tensors (bf16,
     fp16 or fp32, one dtype for all), or a PointerTable from grad_table().
-    out: contiguous fp32 device tensor with plan.S elements (e.g. a row of an
-    [N, S] buffer).  avg: write the mean (sum / N) instead of the sum."""
+    out: contiguous device tensor with plan.S elements (e.g. a row of an
+    [N, S] buffer): float32 for the fp32 shard, bfloat16 for the fp32 result
+    rounded once to bf16.  avg: write the mean (sum / N) instead of the sum."""
     if not isinstance(grads, PointerTable):
         grads = grad_table(plan, grads)
-    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 device tensor")
+    if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_cuda \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 or bfloat16 device tensor")
     if out.numel() != plan.S:
         raise ValueError(f"out has {out.numel()} elements, expected S = {plan.S}")
     flags = _GRAD_FLAG.get(grads.dtype, 0)
     flags |= (SMALL_FOOTPRINT if small else 0) | (AVG if avg else 0)
+    flags |= OUT_BF16 if out.dtype == torch.bfloat16 else 0
     _check(lib().tide_rs(plan.handle, int(rank), grads.array, ctypes.c_void_p(out.data_ptr()),
                          flags, int(max_workgroups), _stream_handle(stream)))
 

@@ -86,7 +86,7 @@ inline void shard_run(const tide_plan *p, int32_t r, int32_t i, int64_t *src, in
 
 // Argument checks shared by the launch paths (host only, no HIP call).
 tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *grads,
-                          const float *out, uint32_t flags, int32_t max_wg);
+                          const void *out, uint32_t flags, int32_t max_wg);
 tide_status check_ag_args(const tide_plan *p, const void *const *rank_src,
                           void *const *params, int32_t elem_bytes, uint32_t flags,
                           int32_t max_wg);

@@ -103,6 +103,10 @@ static_assert(TIDE_RS_RB <= static_cast<int>(kPtrPad) && TIDE_SMALL_RB <= static
 // half of an fp32 pattern, every fp16 value is an fp32 value, fp32 is kept.
 enum GradType { kBf16 = 0, kF16 = 1, kF32 = 2 };
 
+// Output element types of the reduce-scatter: the fp32 result, or that
+// result rounded once to bf16 (nearest, ties to even).
+enum OutType { kOutF32 = 0, kOutBf16 = 1 };
+
 // Everything one TIDE-RS launch needs.  ptrs is the param-major pointer
 // table (entry i*N + r = rank r's gradient of parameter i) plus kPtrPad
 // null entries.  vec_in: every gradient pointer is 16-byte aligned; vec_out:
@@ -114,7 +118,7 @@ struct RsLaunch {
     int64_t ntiles;
     const char *const *ptrs;
     int N, R, avg;
-    float *out;
+    void *out;                   // S elements of the output type
     int vec_in, vec_out;
     unsigned grid;
     int lds;
@@ -137,7 +141,7 @@ struct AgLaunch {
 // Enqueue one launch.  `small` selects the small-footprint tile list's
 // kernel shape (the caller passes that tile list).  Returns the HIP error of
 // the launch (or of allowing its LDS reservation).
-hipError_t launch_rs(const RsLaunch &a, GradType type, bool small);
+hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, bool small);
 hipError_t launch_ag(const AgLaunch &a, bool small);
 
 }  // namespace tide

@@ -75,6 +75,41 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h16)));
 }
 
+// fp32 -> bf16 bits, round to nearest with ties to even, on the pattern:
+// adding 0x7fff plus the lowest kept bit, then cutting the low 16 bits,
+// carries into the kept part exactly when the cut part is above half a
+// unit, or equal to it with an odd kept part.  A carry out of the fraction
+// raises the exponent (to infinity past the largest finite bf16), which is
+// the rounded value.  Subnormals need no special case.  A NaN keeps its top
+// bits with the quiet bit set, so it cannot turn into an infinity.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Output element types of the reduce-scatter: the fp32 sum as is, or
+// rounded once to bf16.
+template <int OT> struct Out;
+template <> struct Out<kOutF32> {
+    static constexpr int ES = 4;
+    typedef f32x4 V4;
+    static __device__ __forceinline__ V4 pack(f32x4 v) { return v; }
+    static __device__ __forceinline__ void one(GLOBAL_AS char *p, float v) {
+        *reinterpret_cast<GLOBAL_AS float *>(p) = v;
+    }
+};
+template <> struct Out<kOutBf16> {
+    static constexpr int ES = 2;
+    typedef u32x2 V4;
+    static __device__ __forceinline__ V4 pack(f32x4 v) {
+        return V4{bf16_rne(v.x) | (bf16_rne(v.y) << 16), bf16_rne(v.z) | (bf16_rne(v.w) << 16)};
+    }
+    static __device__ __forceinline__ void one(GLOBAL_AS char *p, float v) {
+        *reinterpret_cast<GLOBAL_AS uint16_t *>(p) = static_cast<uint16_t>(bf16_rne(v));
+    }
+};
+
 // Per type: element bytes, the vector holding 4 consecutive elements, and
 // the exact widening of such a vector and of one element.  (In a word of
 // two 16-bit elements the lower address sits in the low half.)
@@ -114,19 +149,19 @@ template <> struct Grad<kF32> {
 };
 
 // Scalar path for elements [a, b) of a segment: one lane per element, the
-// same rank-order sum (and mean) as the vector path.  P[r] is rank r's
-// gradient; src is rank R's first element in it.
-template <int IT, int BLOCK>
+// same rank-order sum (and mean, and bf16 rounding) as the vector path.
+// P[r] is rank r's gradient; src is rank R's first element in it; o is the
+// segment's first output element.
+template <int IT, int OT, int BLOCK>
 __device__ __forceinline__ void rs_elems(const char *const *__restrict__ P, int N, int avg,
-                                         int64_t src, float *__restrict__ o, int64_t a,
-                                         int64_t b) {
+                                         int64_t src, GLOBAL_AS char *o, int64_t a, int64_t b) {
     typedef Grad<IT> G;
     for (int64_t k = a + threadIdx.x; k < b; k += BLOCK) {
         const int64_t byte = (src + k) * G::ES;
         float acc = G::one(gload_ptr<char>(P[0] + byte));
         for (int r = 1; r < N; r++) acc = acc + G::one(gload_ptr<char>(P[r] + byte));
         if (avg) acc = acc / static_cast<float>(N);
-        o[k] = acc;
+        Out<OT>::one(o + k * Out<OT>::ES, acc);
     }
 }
 
@@ -194,24 +229,27 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t v, int64_t ntiles) {
 //   k <  L(R,i):  out[off_i + k] = sum_{r=0..N-1} widen(G[r][i][R*seg_i + k])
 //                 (divided by N when avg is set)
 //   k >= L(R,i):  out[off_i + k] = +0.0f   (padding rows, alignment gap)
-// ptrs is param-major: ptrs[i*N + r] = G[r][i].
+// ptrs is param-major: ptrs[i*N + r] = G[r][i].  OT: fp32 output, or the
+// fp32 result rounded to bf16 (padding then +0 in bf16).
 //
 // Lanes take chunks of 4 consecutive elements: 8-byte loads for 16-bit
 // gradients, 16-byte loads for fp32 ones.  vec_in: every gradient pointer is
 // 16-byte aligned, so chunks start where src + k is a multiple of 4; the few
 // elements before the first and after the last chunk of a tile take the
-// scalar path.  vec_out: `out` is 16-byte aligned; a chunk's 4 fp32 results
-// go out as one 16-byte store when its output offset is a multiple of 4 too,
-// so every store instruction of a wave covers one contiguous 1 KiB span.
+// scalar path.  vec_out: `out` is 16-byte aligned; a chunk's 4 results go
+// out as one 16-byte (fp32) or 8-byte (bf16) store when its output offset is
+// a multiple of 4 too, so every store instruction of a wave covers one
+// contiguous span.
 // PACE > 0 makes each wave sleep between tiles.
-template <int IT, int BLOCK, int CPL, int RB, int PACE, bool XMAP, int64_t TILE>
+template <int IT, int OT, int BLOCK, int CPL, int RB, int PACE, bool XMAP, int64_t TILE>
 __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__ pdesc,
                                                    const Tile *__restrict__ tiles,
                                                    int64_t ntiles,
                                                    const char *const *__restrict__ ptrs,
-                                                   int N, int R, int avg, float *__restrict__ out,
+                                                   int N, int R, int avg, void *__restrict__ out,
                                                    int vec_in, int vec_out) {
     constexpr int ES = Grad<IT>::ES;
+    typedef Out<OT> O;
     for (int64_t v = blockIdx.x; v < ntiles; v += gridDim.x) {
         const Tile tile = tiles[XMAP ? xcd_tile(v, ntiles) : v];
         const ParamDesc d = pdesc[tile.param];
@@ -221,7 +259,7 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
         const int64_t kb = tile.k0;
         const int64_t ke = min(kb + TILE, d.span);
         const int64_t re = min(ke, L);
-        float *__restrict__ o = out + d.off;
+        GLOBAL_AS char *o = gstore_ptr<char>(out) + d.off * O::ES;
         const char *const *__restrict__ P = ptrs + static_cast<int64_t>(tile.param) * N;
 
         if (kb < re) {
@@ -230,14 +268,14 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
                 vs = min(re, kb + ((4 - ((src + kb) & 3)) & 3));
                 ve = vs + ((re - vs) & ~static_cast<int64_t>(3));
             }
-            rs_elems<IT, BLOCK>(P, N, avg, src, o, kb, vs);
-            rs_elems<IT, BLOCK>(P, N, avg, src, o, ve, re);
+            rs_elems<IT, OT, BLOCK>(P, N, avg, src, o, kb, vs);
+            rs_elems<IT, OT, BLOCK>(P, N, avg, src, o, ve, re);
 
             // A tile holds at most TILE/4 chunks, so every per-lane byte
             // offset below fits in 32 bits.
             const int nch = static_cast<int>((ve - vs) >> 2);
             const bool st16 = vec_out && (((d.off + vs) & 3) == 0);
-            GLOBAL_AS char *obase = gstore_ptr<char>(o + vs);
+            GLOBAL_AS char *obase = o + vs * O::ES;
             for (int c0 = 0; c0 < nch; c0 += BLOCK * CPL) {
                 uint32_t in_off[CPL], out_off[CPL];
                 bool ok[CPL];
@@ -249,7 +287,7 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
                     // and do not store.
                     const uint32_t c = static_cast<uint32_t>(ok[j] ? ch : nch - 1);
                     in_off[j] = c * (4u * ES);
-                    out_off[j] = c * 16u;
+                    out_off[j] = c * (4u * O::ES);
                 }
                 f32x4 acc[CPL];
                 const int64_t first_byte = (src + vs) * ES;
@@ -266,16 +304,16 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
                 for (int j = 0; j < CPL; j++) {
                     if (!ok[j]) continue;
                     if (st16) {
-                        stream_store(acc[j], reinterpret_cast<GLOBAL_AS f32x4 *>(obase + out_off[j]));
+                        stream_store(O::pack(acc[j]),
+                                     reinterpret_cast<GLOBAL_AS typename O::V4 *>(obase + out_off[j]));
                     } else {
-                        GLOBAL_AS float *dst = reinterpret_cast<GLOBAL_AS float *>(obase + out_off[j]);
 #pragma unroll
-                        for (int e = 0; e < 4; e++) dst[e] = acc[j][e];
+                        for (int e = 0; e < 4; e++) O::one(obase + out_off[j] + e * O::ES, acc[j][e]);
                     }
                 }
             }
         }
-        for (int64_t k = max(kb, L) + threadIdx.x; k < ke; k += BLOCK) o[k] = 0.0f;
+        for (int64_t k = max(kb, L) + threadIdx.x; k < ke; k += BLOCK) O::one(o + k * O::ES, 0.0f);
         if (PACE > 0) {
 #pragma unroll
             for (int p = 0; p < PACE; p++) __builtin_amdgcn_s_sleep(32);
@@ -386,11 +424,12 @@ hipError_t allow_lds(const void *kernel, int bytes) {
 
 // Default launches: one 256-lane workgroup per 4096-element tile.  Small-
 // footprint launches: the small tile list and its kernel shape.
-template <int IT, bool SMALL>
+template <int IT, int OT, bool SMALL>
 hipError_t launch_rs_t(const RsLaunch &a) {
-    auto k = SMALL ? rs_kernel<IT, TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_RB, TIDE_SMALL_PACE,
-                               TIDE_XMAP_RS, kRsTileSmall>
-                   : rs_kernel<IT, kBlock, kRsChunksPerLane, TIDE_RS_RB, 0, TIDE_XMAP_RS, kRsTile>;
+    auto k = SMALL ? rs_kernel<IT, OT, TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_RB,
+                               TIDE_SMALL_PACE, TIDE_XMAP_RS, kRsTileSmall>
+                   : rs_kernel<IT, OT, kBlock, kRsChunksPerLane, TIDE_RS_RB, 0, TIDE_XMAP_RS,
+                               kRsTile>;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(k), a.lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_BLOCK : kBlock), a.lds, a.stream,
@@ -411,15 +450,21 @@ hipError_t launch_ag_t(const AgLaunch &a) {
     return hipGetLastError();
 }
 
+template <int OT>
+hipError_t launch_rs_o(const RsLaunch &a, GradType type, bool small) {
+    switch (type) {
+    case kF32: return small ? launch_rs_t<kF32, OT, true>(a) : launch_rs_t<kF32, OT, false>(a);
+    case kF16: return small ? launch_rs_t<kF16, OT, true>(a) : launch_rs_t<kF16, OT, false>(a);
+    default: return small ? launch_rs_t<kBf16, OT, true>(a) : launch_rs_t<kBf16, OT, false>(a);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_rs(const RsLaunch &a, GradType type, bool small) {
+hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, bool small) {
     (void)hipGetLastError();
-    switch (type) {
-    case kF32: return small ? launch_rs_t<kF32, true>(a) : launch_rs_t<kF32, false>(a);
-    case kF16: return small ? launch_rs_t<kF16, true>(a) : launch_rs_t<kF16, false>(a);
-    default: return small ? launch_rs_t<kBf16, true>(a) : launch_rs_t<kBf16, false>(a);
-    }
+    return out == kOutBf16 ? launch_rs_o<kOutBf16>(a, type, small)
+                           : launch_rs_o<kOutF32>(a, type, small);
 }
 
 hipError_t launch_ag(const AgLaunch &a, bool small) {

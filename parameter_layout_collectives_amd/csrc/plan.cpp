@@ -62,7 +62,7 @@ void clear_error() { g_last_error.clear(); }
 const char *last_error_cstr() { return g_last_error.c_str(); }
 
 tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *grads,
-                          const float *out, uint32_t flags, int32_t max_wg) {
+                          const void *out, uint32_t flags, int32_t max_wg) {
     if (!p) return fail(TIDE_E_INVALID, "tide_rs: plan is NULL");
     if (rank < 0 || rank >= p->N)
         return fail(TIDE_E_INVALID, "tide_rs: rank " + std::to_string(rank) +
@@ -70,21 +70,23 @@ tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *g
     if (flags & TIDE_F_COPY_ENGINE)
         return fail(TIDE_E_UNSUPPORTED,
                     "tide_rs: TIDE_F_COPY_ENGINE is for tide_ag (a reduction needs arithmetic)");
-    if (flags & ~(TIDE_F_SMALL_FOOTPRINT | TIDE_F_AVG | TIDE_F_GRAD_F16 | TIDE_F_GRAD_F32))
+    if (flags & ~(TIDE_F_SMALL_FOOTPRINT | TIDE_F_AVG | TIDE_F_GRAD_F16 | TIDE_F_GRAD_F32 |
+                  TIDE_F_OUT_BF16))
         return fail(TIDE_E_UNSUPPORTED, "tide_rs: unknown flag bits");
     if ((flags & TIDE_F_GRAD_F16) && (flags & TIDE_F_GRAD_F32))
         return fail(TIDE_E_INVALID, "tide_rs: TIDE_F_GRAD_F16 and TIDE_F_GRAD_F32 both set");
     const uintptr_t es = (flags & TIDE_F_GRAD_F32) ? 4u : 2u;
+    const uintptr_t os = (flags & TIDE_F_OUT_BF16) ? 2u : 4u;
     if (max_wg < 0) return fail(TIDE_E_INVALID, "tide_rs: max_workgroups < 0");
     if (p->S == 0) return TIDE_OK;
     if (!grads) return fail(TIDE_E_INVALID, "tide_rs: grads array is NULL");
     if (!out) return fail(TIDE_E_INVALID, "tide_rs: out is NULL");
-    if (reinterpret_cast<uintptr_t>(out) & 3)
-        return fail(TIDE_E_INVALID, "tide_rs: out is not 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(out) % os)
+        return fail(TIDE_E_INVALID, "tide_rs: out is not aligned to its element size");
     // One pass over the N*P gradient runs rank `rank` reads (no allocation):
     // each must be non-null, element-aligned and disjoint from `out`.
     const uintptr_t o = reinterpret_cast<uintptr_t>(out);
-    const Span written{o, o + static_cast<uintptr_t>(p->S) * 4u};
+    const Span written{o, o + static_cast<uintptr_t>(p->S) * os};
     for (int32_t i = 0; i < p->P; i++) {
         int64_t src, L;
         shard_run(p, rank, i, &src, &L);

@@ -360,7 +360,7 @@ void release_device_states(const tide_plan *p) {
 using tide::fail;
 
 extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *const *grads,
-                               float *out, uint32_t flags, int32_t max_workgroups,
+                               void *out, uint32_t flags, int32_t max_workgroups,
                                void *stream) {
     tide_status st = tide::check_rs_args(plan, rank, grads, out, flags, max_workgroups);
     if (st != TIDE_OK) return st;
@@ -406,7 +406,8 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
     const tide::GradType type = (flags & TIDE_F_GRAD_F32)   ? tide::kF32
                                 : (flags & TIDE_F_GRAD_F16) ? tide::kF16
                                                             : tide::kBf16;
-    hipError_t e = tide::launch_rs(L, type, small);
+    const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
+    hipError_t e = tide::launch_rs(L, type, otype, small);
     if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
     st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
     if (st != TIDE_OK) return st;

@@ -53,6 +53,25 @@ def same_f32(got, want):
     return np.array_equal(g[~gn].view(np.uint32), w[~wn].view(np.uint32))
 
 
+def same_bf16(got, want):
+    """Bitwise equality of bf16 bit patterns (uint16), NaNs by class only."""
+    g = np.asarray(got, np.uint16)
+    w = np.asarray(want, np.uint16)
+    gn = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+    wn = ((w & 0x7F80) == 0x7F80) & ((w & 0x7F) != 0)
+    return np.array_equal(gn, wn) and np.array_equal(g[~gn], w[~wn])
+
+
+def first_mismatch16(got, want):
+    g = np.asarray(got, np.uint16)
+    w = np.asarray(want, np.uint16)
+    idx = np.nonzero(g != w)[0]
+    if idx.size == 0:
+        return None
+    k = int(idx[0])
+    return k, hex(int(g[k])), hex(int(w[k])), int(idx.size)
+
+
 def first_mismatch(got, want):
     g = np.asarray(got, np.float32).view(np.uint32)
     w = np.asarray(want, np.float32).view(np.uint32)

@@ -145,7 +145,14 @@ def test_rs_argument_errors():
     # fp32 gradients read 4 bytes per element: out at 16 bytes into rank 1's
     # first gradient overlaps elements 4..7 only when they are 4 bytes wide
     assert _rs(plan, 0, good, A + 0x20000 + 16, flags=0x10) == E_INVALID
-    assert _rs(plan, 0, good, out, flags=0x20) == E_UNSUPPORTED
+    assert _rs(plan, 0, good, out, flags=0x40) == E_UNSUPPORTED
+    # bf16 output: 2-byte elements, so an odd address is misaligned; the
+    # written span is 2*S = 24 bytes, so out 8 bytes before the elements read
+    # from rank 1's first gradient overlaps them.
+    assert _rs(plan, 0, good, out + 1, flags=0x20) == E_INVALID
+    assert b"aligned" in L.tide_last_error()
+    assert _rs(plan, 0, good, A + 0x20000 - 8, flags=0x20) == E_INVALID
+    assert b"overlaps" in L.tide_last_error()
 
 
 def test_rs_empty_plan_is_a_noop():

@@ -10,7 +10,8 @@ Workloads (architecture shapes only, synthetic seeded bf16 gradients):
 
 The whole fp32 output block of each checked rank is compared bit for bit
 with the oracle, which reads host copies of exactly the gradient slices the
-rank reduces.  The all-gather placement is compared on every element of
+rank reduces; so is the bf16 block (the fp32 result rounded once, the
+oracle's rounding applied to its fp32 block).  The all-gather placement is compared on every element of
 every parameter.
 """
 import gc
@@ -22,7 +23,7 @@ import torch
 import parameter_layout_collectives_amd as tide
 import workloads
 from gpu_helpers import (BF16_SENTINEL, F32_SENTINEL, bits16, expected_rs, first_mismatch,
-                         note, same_f32)
+                         first_mismatch16, note, same_bf16, same_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,8 +44,10 @@ def _free():
 
 def _rs_cases(orc, w, grads, plan, table, ranks, modes):
     out = torch.empty(plan.S, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(plan.S, dtype=torch.bfloat16, device=DEV)
     for R in ranks:
         want = expected_rs(orc, w.shapes, w.world, R, grads, plan)
+        want16 = orc.round_bf16(want)
         for small in modes:
             out.view(torch.int32).fill_(F32_SENTINEL)
             note(f"{w.name}: tide_rs R={R} small={small}")
@@ -52,6 +55,13 @@ def _rs_cases(orc, w, grads, plan, table, ranks, modes):
             torch.cuda.synchronize()
             got = out.cpu().numpy()
             assert same_f32(got, want), (w.name, R, small, first_mismatch(got, want))
+            out16.view(torch.int16).fill_(BF16_SENTINEL)
+            note(f"{w.name}: tide_rs bf16 out R={R} small={small}")
+            tide.rs(plan, R, table, out16, small=small)
+            torch.cuda.synchronize()
+            got16 = bits16(out16)
+            assert same_bf16(got16, want16), (w.name, R, small, first_mismatch16(got16, want16))
+    del out16
     return out
 
 

@@ -17,7 +17,7 @@ import torch
 import parameter_layout_collectives_amd as tide
 import workloads
 from gpu_helpers import (BF16_SENTINEL, F32_SENTINEL, bits16, bits32, expected_rs,
-                         first_mismatch, note, run_rs, same_f32)
+                         first_mismatch, first_mismatch16, note, run_rs, same_bf16, same_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -279,6 +279,95 @@ def test_f16_special_values(orc):
     for R in range(N):
         for avg in (False, True):
             check_rs_typed(orc, [(n // 4, 4)], N, grads, R, "f16", avg)
+
+
+# ---------------------------------------------------------------------------
+# reduce-scatter with a bf16 shard (the fp32 result rounded once)
+# ---------------------------------------------------------------------------
+
+def check_rs_bf16(orc, shapes, N, grads, R, dtype="bf16", avg=False, align=1, out_shift=0,
+                  **kw):
+    """tide_rs into a bf16 block `out_shift` elements into a sentinel-filled
+    buffer; compared with the oracle's fp32 block rounded by the oracle."""
+    plan = tide.Plan(shapes, N, align)
+    base = torch.full((plan.S + out_shift + 1,), BF16_SENTINEL, dtype=torch.int16,
+                      device=DEV).view(torch.bfloat16)
+    out = base[out_shift:out_shift + plan.S]
+    note(f"tide_rs bf16 out {dtype} avg={avg} shapes={shapes} N={N} R={R} align={align} "
+         f"out_shift={out_shift} {kw}")
+    run_rs(plan, R, grads, out, avg=avg, **kw)
+    slices = [[host_elems(g.reshape(-1)[plan.real(R, i)[0]:plan.real(R, i)[0] +
+                                        plan.real(R, i)[1]], dtype)
+               for i, g in enumerate(rank)] for rank in grads]
+    want = orc.round_bf16(orc.rs_slices(shapes, N, R, slices, align=align, dtype=dtype, avg=avg))
+    got = bits16(out)
+    assert same_bf16(got, want), (dtype, avg, R, first_mismatch16(got, want))
+    whole = bits16(base)
+    assert np.all(whole[:out_shift] == BF16_SENTINEL) and whole[-1] == BF16_SENTINEL
+
+
+def test_bf16_out_tiny_every_rank(orc):
+    w = workloads.WORKLOADS["tiny"]
+    g = to_dev(workloads.all_grads(w))
+    for R in range(w.world):
+        for kw in ({}, {"small": True}, {"max_workgroups": 1}):
+            for avg in (False, True):
+                check_rs_bf16(orc, w.shapes, w.world, g, R, avg=avg, **kw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("N", [1, 3, 8, 16])
+def test_bf16_out_ragged(orc, dtype, N):
+    g = typed_grads(RAGGED[0], N, 500 + N, dtype)
+    for R in sorted({0, N // 2, N - 1}):
+        check_rs_bf16(orc, RAGGED[0], N, g, R, dtype=dtype)
+        check_rs_bf16(orc, RAGGED[0], N, g, R, dtype=dtype, avg=True, small=True)
+    g1 = typed_grads(RAGGED[1], N, 600 + N, dtype)
+    check_rs_bf16(orc, RAGGED[1], N, g1, N - 1, dtype=dtype, align=8)
+
+
+@pytest.mark.parametrize("out_shift", [1, 4, 8])
+def test_bf16_out_unaligned(orc, out_shift):
+    """Outputs 2-, 8- and 16-byte aligned (scalar and vector stores), and
+    gradients at odd element offsets (scalar loads)."""
+    shapes = [(1031, 3), (9000,), (5, 5)]
+    N = 4
+    g = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=700))
+    check_rs_bf16(orc, shapes, N, g, 1, out_shift=out_shift)
+    bufs = [[torch.empty(t.numel() + 1, dtype=torch.bfloat16, device=DEV) for t in rank]
+            for rank in g]
+    odd = []
+    for rank, brank in zip(g, bufs):
+        row = []
+        for t, b in zip(rank, brank):
+            b[1:].copy_(t.reshape(-1))
+            row.append(b[1:].view(t.shape))
+        odd.append(row)
+    check_rs_bf16(orc, shapes, N, odd, 2, out_shift=out_shift, avg=True)
+
+
+def test_bf16_out_rounding_edges(orc):
+    """Sums on rounding ties (integer values past 256, where bf16 steps by
+    2 and 4), sums that round to infinity, subnormal sums, NaN and Inf."""
+    N = 3
+    shapes = [(4096,), (517,)]
+    rng = np.random.default_rng(808)
+    ints = [[torch.from_numpy(rng.integers(-300, 301, size=s).astype(np.float32))
+             .to(torch.bfloat16).to(DEV) for s in shapes] for _ in range(N)]
+    for R in range(N):
+        check_rs_bf16(orc, shapes, N, ints, R)
+    big = 3.3999e38        # above the largest bf16 by more than half its unit
+    vals = np.array([big, -big, 3.3895e38, 1e-39, 3e-40, -5e-41, np.inf, -np.inf, np.nan,
+                     1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 0.0], np.float32)
+    # rank 0 cycles through the values, rank 1 adds zeros, rank 2 a rotation
+    # of them, so every pair of values meets somewhere
+    f32 = [[torch.from_numpy(np.resize(vals, 4096)).to(DEV),
+            torch.from_numpy(np.resize(vals[::-1].copy(), 517)).to(DEV)],
+           [torch.zeros(4096, device=DEV), torch.zeros(517, device=DEV)],
+           [torch.from_numpy(np.resize(np.roll(vals, 5), 4096)).to(DEV),
+            torch.from_numpy(np.resize(np.roll(vals, 3), 517)).to(DEV)]]
+    for R in range(N):
+        check_rs_bf16(orc, shapes, N, f32, R, dtype="f32")
 
 
 # ---------------------------------------------------------------------------
