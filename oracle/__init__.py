@@ -15,6 +15,10 @@ What it computes (cited by page title and section):
     analysis" §"分片中的通信原语").
   * ``rs_traffic``: elements pulled from peers, (N-1)/N*Psi per rank on
     average (apxml "Communication volume analysis" §"带宽饱和和节点扩展").
+  * ``pack``: one rank's per-parameter tensors laid out rank-major (the
+    all-gather buffer's layout), padding and gaps zero: the staging of the
+    two-stage reduce-scatter (TIDE article §"TIDE的设计思路", two-stage
+    pipeline and Slot-Reuse).
   * ``round_bf16``: fp32 -> bf16, round to nearest, ties to even; a bf16
     shard is the fp32 block from ``rs`` rounded once (the reduction itself
     stays fp32: tqpw.cn blog §3.2, TIDE article §"TIDE的设计思路").
@@ -102,10 +106,11 @@ class Oracle:
         lib.oracle_rs_traffic.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_round_bf16.argtypes = [_p, _p, _i64]
+        lib.oracle_pack.argtypes = [_i32, _i32, _p, _p, _i64, _i32, _p, _p]
         for fn in (lib.oracle_geometry, lib.oracle_shard_run, lib.oracle_rs,
                    lib.oracle_rs_slices, lib.oracle_rs_typed, lib.oracle_rs_slices_typed,
                    lib.oracle_ag, lib.oracle_rs_traffic, lib.oracle_threads,
-                   lib.oracle_round_bf16):
+                   lib.oracle_round_bf16, lib.oracle_pack):
             fn.restype = ctypes.c_int
         lib.oracle_set_threads.restype = None
         self.lib = lib
@@ -232,6 +237,25 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_ag: invalid arguments")
         return params
+
+    def pack(self, shapes, N, tensors, elem_bytes=2, align=1):
+        """tensors[i]: one rank's tensor of param i (uint16 bits for 2-byte,
+        uint32 for 4-byte elements).  Returns its rank-major slot (N*S,)."""
+        P = len(shapes)
+        g = self.geometry(shapes, N, align)
+        dt = {2: np.uint16, 4: np.uint32}[elem_bytes]
+        src = []
+        for i in range(P):
+            a = np.ascontiguousarray(tensors[i]).view(dt).reshape(-1)
+            assert a.size == g.numel(i), (i, a.size, g.numel(i))
+            src.append(a)
+        slot = np.empty(N * g.S, dt)
+        d0, inner = self._dims(shapes)
+        rc = self.lib.oracle_pack(N, P, d0.ctypes.data, inner.ctypes.data, align, elem_bytes,
+                                  self._ptrs(src), slot.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_pack: invalid arguments")
+        return slot
 
     def rs_traffic(self, shapes, N, R, align=1):
         """(real, padded) element counts rank R pulls from its N-1 peers."""

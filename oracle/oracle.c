@@ -281,6 +281,44 @@ int oracle_rs_slices(int32_t N, int32_t P, const int64_t *d0, const int64_t *inn
 }
 
 /* ---------------------------------------------------------------------- */
+/* Staging for the two-stage reduce-scatter ([TIDE] §"TIDE的设计思路": the  */
+/* pipeline stages gradients, optionally in vacated all-gather slots).      */
+/* ---------------------------------------------------------------------- */
+
+/* One rank's per-parameter tensors laid out rank-major, as the all-gather
+ * buffer is: for every destination rank q, parameter i and k < seg_i
+ *   slot[q*S + off_i + k] = tensors[i][src(q,i) + k]   if k < L(q,i)
+ *                         = 0                           otherwise (padding),
+ * and every alignment gap is 0.  elem_bytes-byte elements, copied exactly.
+ * Block q of the slot is what this rank contributes to rank q's shard. */
+int oracle_pack(int32_t N, int32_t P, const int64_t *d0, const int64_t *inner,
+                int64_t align, int32_t elem_bytes, const void *const *tensors, void *slot)
+{
+    int64_t S;
+    if (N <= 0 || P <= 0 || (elem_bytes != 2 && elem_bytes != 4)) return ORACLE_EINVAL;
+    int64_t *c = malloc(3 * sizeof(int64_t) * (size_t)P);
+    if (!c) return ORACLE_EINVAL;
+    int64_t *seg = c + P, *off = c + 2 * P;
+    if (oracle_geometry(N, P, d0, inner, align, c, seg, off, &S) != ORACLE_OK) {
+        free(c);
+        return ORACLE_EINVAL;
+    }
+    /* Everything starts as zero: padding rows and gaps keep it. */
+    memset(slot, 0, (size_t)N * (size_t)S * (size_t)elem_bytes);
+    for (int32_t q = 0; q < N; q++) {
+        for (int32_t i = 0; i < P; i++) {
+            int64_t src, L;
+            shard_run(q, d0[i], inner[i], c[i], &src, &L);
+            char *to = (char *)slot + ((int64_t)q * S + off[i]) * elem_bytes;
+            const char *from = (const char *)tensors[i] + src * elem_bytes;
+            if (L > 0) memcpy(to, from, (size_t)L * (size_t)elem_bytes);
+        }
+    }
+    free(c);
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------- */
 /* fp32 -> bf16 rounding of a reduced shard.                               */
 /* ---------------------------------------------------------------------- */
 

@@ -63,6 +63,12 @@ MUTANTS = {
                               "if (isnan(x)) return (uint16_t)(u >> 16);"),
     "round_overflow_saturates": ("double aup = ((up & 0x7fffu) == 0x7f80u) ? ldexp(1.0, 128)",
                                  "if ((up & 0x7fffu) == 0x7f80u) return t;\n    double aup = 0 ? 0"),
+    "pack_pads_with_ones": ("memset(slot, 0, (size_t)N * (size_t)S * (size_t)elem_bytes);",
+                            "memset(slot, 1, (size_t)N * (size_t)S * (size_t)elem_bytes);"),
+    "pack_previous_offset": ("char *to = (char *)slot + ((int64_t)q * S + off[i]) * elem_bytes;",
+                             "char *to = (char *)slot + ((int64_t)q * S + (i ? off[i - 1] : 0)) * elem_bytes;"),
+    "pack_ignores_owner": ("const char *from = (const char *)tensors[i] + src * elem_bytes;",
+                           "const char *from = (const char *)tensors[i];"),
     "f32_read_as_half_width": ("memcpy(&f, (const char *)run + 4 * k, sizeof f);",
                                "memcpy(&f, (const char *)run + 2 * k, sizeof f);"),
 }

@@ -22,6 +22,10 @@ Pins used (none of them re-types the oracle's formulas):
     numpy does, N=2 and integer-valued sums of fp16/fp32 gradients, the mean
     as an exact power-of-two scaling (N = 2^k) or as the exact rational
     sum/N rounded to nearest even (other N);
+  * staging for the two-stage reduce-scatter: the packed slot equals the
+    brute-force rank blocks of the tensors (zero padding), the all-gather
+    of a packed slot gives the tensors back, and the reduce-scatter of the
+    staged blocks equals the one-pass reduce-scatter of the gradients;
   * fp32 -> bf16 rounding of a shard: torch's own conversion over millions
     of patterns (every low half under chosen high halves), a search over all
     65,536 bf16 values for the nearest one, worked ties, and an N=2 shard
@@ -397,6 +401,57 @@ def pin_mean_exact_rounding(orc):
                 want = brute.round_f32(Fraction(float(s_[k])) / N)
                 assert bits_f32([m[k]])[0] == bits_f32([want])[0], (N, R, k)
             assert np.all(bits_f32(m[L:g.seg[0]]) == 0)          # padding stays +0
+
+
+# --------------------------------------------------------------------------
+# staging (two-stage reduce-scatter)
+# --------------------------------------------------------------------------
+
+def pin_pack_vs_brute(orc):
+    rng = np.random.default_rng(910)
+    for shapes in SWEEP:
+        for N in (1, 2, 3, 5, 8):
+            for align in (1, 4):
+                ts = []
+                for s in shapes:
+                    n = int(np.prod(s)) if len(s) else 1
+                    ts.append(rng.integers(1, 65535, size=n).astype(np.uint16))
+                got = orc.pack(shapes, N, ts, align=align)
+                tt = [torch.from_numpy(t.astype(np.int64)).reshape(s) for t, s in zip(ts, shapes)]
+                want = torch.cat([brute.rank_block(tt, N, q, align, pad_value=0)
+                                  for q in range(N)]).numpy().astype(np.uint16)
+                assert np.array_equal(got, want), (shapes, N, align)
+
+
+def pin_ag_inverts_pack(orc):
+    rng = np.random.default_rng(911)
+    for shapes in SWEEP:
+        for N in (1, 3, 8):
+            for e, dt in ((2, np.uint16), (4, np.uint32)):
+                ts = [rng.integers(0, 2 ** (8 * e) - 1, size=int(np.prod(s)) if len(s) else 1,
+                                   dtype=np.uint64).astype(dt) for s in shapes]
+                slot = orc.pack(shapes, N, ts, elem_bytes=e, align=3)
+                g = orc.geometry(shapes, N, 3)
+                back = orc.ag(shapes, N, [slot[q * g.S:(q + 1) * g.S] for q in range(N)],
+                              elem_bytes=e, align=3)
+                for i in range(len(shapes)):
+                    assert np.array_equal(back[i], ts[i]), (shapes, N, e, i)
+
+
+def pin_two_stage_is_one_pass(orc):
+    # reduce-scatter of block R of every rank's staged slot == reduce-scatter
+    # of the gradients themselves, for every rank R
+    for shapes in SWEEP[:4]:
+        for N in (2, 3, 4):
+            grads = _rand_case(shapes, N, 920 + N)
+            g = orc.geometry(shapes, N)
+            slots = [orc.pack(shapes, N, grads[r]) for r in range(N)]
+            for R in range(N):
+                slices = [[slots[r][R * g.S + g.off[i]:R * g.S + g.off[i] + g.run(R, i)[1]]
+                           for i in range(len(shapes))] for r in range(N)]
+                a = orc.rs_slices(shapes, N, R, slices)
+                b = orc.rs(shapes, N, R, grads)
+                assert np.array_equal(bits_f32(a), bits_f32(b)), (shapes, N, R)
 
 
 # --------------------------------------------------------------------------
