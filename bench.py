@@ -183,6 +183,46 @@ def rs_variants(step, reps=20, warmup=3):
     return res
 
 
+def two_stage_leg(step, reps=16, warmup=2):
+    """One GPU's share of the two-stage TIDE-RS on the step's workload, R
+    rotating: stage 1 packs rank R's gradients into its rank-major slot
+    (2*Psi bytes read, 2*N*S written), stage 2 reduces block R of the N
+    slots (the peers' slots are packed beforehand, untimed).  Staging needs
+    N*S*2 bytes per rank, or none with Slot-Reuse (the vacated all-gather
+    buffer has exactly that size)."""
+    plan, N, S = step.plan, step.w.world, step.plan.S
+    slots = torch.empty(N, N * S, dtype=torch.bfloat16, device="cuda")
+    tables = [tide.PointerTable(step.grads[r], torch.bfloat16) for r in range(N)]
+    for r in range(N):
+        tide.pack(plan, tables[r], slots[r])
+    stable = tide.slot_table(plan, slots)
+    out = step.blocks
+    for k in range(warmup):
+        tide.pack(plan, tables[k % N], slots[k % N])
+        tide.rs_slots(plan, k % N, stable, out[k % N])
+    ev1, ev2 = timed_events(reps), timed_events(reps)
+    torch.cuda.synchronize()
+    for k in range(reps):
+        R = k % N
+        ev1[k][0].record()
+        tide.pack(plan, tables[R], slots[R])
+        ev1[k][1].record()
+        ev2[k][0].record()
+        tide.rs_slots(plan, R, stable, out[R])
+        ev2[k][1].record()
+    torch.cuda.synchronize()
+    b1 = 2 * step.w.psi + 2 * N * S
+    st1 = kernel_stats("tide_pack", b1, [a.elapsed_time(b) * 1e-3 for a, b in ev1])
+    st2 = kernel_stats("tide_rs_slots", step.b_rs, [a.elapsed_time(b) * 1e-3 for a, b in ev2])
+    t = st1["mean_us"] + st2["mean_us"]
+    log(f"two-stage: pack {st1['GBps']:.1f} GB/s, rs_slots {st2['GBps']:.1f} GB/s, "
+        f"{t:.1f} us per rank vs one-pass")
+    del slots, stable, tables
+    return {"stage1_pack": st1, "stage2_rs_slots": st2, "total_us": t,
+            "rs_effective_GBps": step.b_rs / (t * 1e-6) / 1e9,
+            "staging_bytes_per_rank": 2 * N * S, "staging_bytes_with_slot_reuse": 0}
+
+
 def kernel_stats(name, nbytes, times):
     mean = statistics.fmean(times)
     q = sorted(times)
@@ -443,7 +483,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the tide_rs flag variants (bf16 shard, mean)")
+                    help="skip the tide_rs flag variants (bf16 shard, mean) and the "
+                         "two-stage reduce-scatter")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -486,6 +527,7 @@ def main():
     }
 
     variants = None if args.no_variants else rs_variants(step)
+    two_stage = None if args.no_variants else two_stage_leg(step)
     copy_gbps = None if args.no_copy else copy_ceiling()
     if copy_gbps:
         log(f"copy ceiling {copy_gbps:.1f} GB/s")
@@ -537,6 +579,7 @@ def main():
         "tide_rs": rs_k,
         "tide_ag": ag_k,
         "tide_rs_variants": variants,
+        "two_stage_rs": two_stage,
         "corun": corun_res,
         "corun_ag": corun_ag_res,
         "gemm_slowdown_pct": None if not corun_res else {

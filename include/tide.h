@@ -209,6 +209,44 @@ tide_status tide_ag(const tide_plan *plan, const void *const *rank_src,
                     int32_t max_workgroups, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Two-stage TIDE-RS with Slot-Reuse (TIDE article §"TIDE的设计思路": the  */
+/* two-stage pipeline separates gradient reads from network progress, and  */
+/* Slot-Reuse stages gradients in vacated all-gather slots).               */
+/* ---------------------------------------------------------------------- */
+
+/* Stage 1: lay one rank's per-parameter tensors out rank-major in a staging
+ * slot of N*S elements - the layout of the all-gather buffer, so a vacated
+ * all-gather buffer can serve as the slot:
+ *   slot[q*S + off_i + k] = tensors[i][src(q,i) + k]   for k < L(q,i)
+ *   slot[q*S + off_i + k] = 0 for L(q,i) <= k < seg_i, and gaps are 0,
+ * for every destination rank q.  Block q is this rank's contribution to
+ * rank q's shard.  An exact copy of elem_bytes-byte elements.
+ *   tensors     host array of P device pointers (dim0_i*inner_i elements;
+ *               NULL allowed when that is 0), element-aligned.
+ *   slot        device pointer to N*S elements, element-aligned; it must not
+ *               overlap any tensor.
+ *   elem_bytes  2 (bf16/fp16) or 4 (fp32).
+ *   flags       0 or TIDE_F_SMALL_FOOTPRINT; other bits -> TIDE_E_UNSUPPORTED.
+ *   max_workgroups, stream  as for tide_rs. */
+tide_status tide_pack(const tide_plan *plan, const void *const *tensors, void *slot,
+                      int32_t elem_bytes, uint32_t flags, int32_t max_workgroups,
+                      void *stream);
+
+/* Stage 2: rank `rank`'s block of the reduce-scatter from N staged slots:
+ *   out[off_i + k] = rank-order fp32 sum over r of widen(slots[r][rank*S + off_i + k])
+ * for k < L(rank,i), and +0 elsewhere - bit-identical to tide_rs over the
+ * gradients the slots were packed from (same order, same widening, and the
+ * same flags: TIDE_F_SMALL_FOOTPRINT, TIDE_F_AVG, TIDE_F_OUT_BF16, and
+ * TIDE_F_GRAD_F16 / TIDE_F_GRAD_F32 for the slot element type).
+ *   slots   host array of N device pointers; slots[r] = rank r's slot (N*S
+ *           elements, aligned to the element size).  Only block `rank` of
+ *           each slot is read, and of it only the real elements.
+ *   out     as for tide_rs; must not overlap any element that is read.
+ * Errors and streams as for tide_rs. */
+tide_status tide_rs_slots(const tide_plan *plan, int32_t rank, const void *const *slots,
+                          void *out, uint32_t flags, int32_t max_workgroups, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Diagnostics.                                                            */
 /* ---------------------------------------------------------------------- */
 

@@ -218,7 +218,79 @@ def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, table
                          _stream_handle(stream)))
 
 
+def _slot_size_ok(plan, slot, what):
+    if not slot.is_cuda or not slot.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous device tensor")
+    if slot.numel() != plan.world * plan.S:
+        raise ValueError(f"{what} has {slot.numel()} elements, expected N*S = "
+                         f"{plan.world * plan.S}")
+
+
+def pack(plan, tensors, slot, small=False, max_workgroups=0, stream=None):
+    """Stage 1 of the two-stage TIDE-RS: lay one rank's per-parameter tensors
+    out rank-major in `slot` (N*S elements of the tensors' dtype; for
+    Slot-Reuse, the vacated all-gather buffer).  Padding and gaps become 0.
+
+    tensors: list of P device tensors of one 2- or 4-byte dtype, or a
+    PointerTable of them."""
+    if not isinstance(tensors, PointerTable):
+        if len(tensors) != plan.P:
+            raise ValueError(f"expected {plan.P} tensors, got {len(tensors)}")
+        for i, t in enumerate(tensors):
+            if t.dtype != slot.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"tensors[{i}] must be a contiguous {slot.dtype} device tensor")
+            if t.numel() != _numel(plan.shapes[i]):
+                raise ValueError(f"tensors[{i}] has {t.numel()} elements, "
+                                 f"expected {_numel(plan.shapes[i])}")
+        tensors = PointerTable(tensors, slot.dtype)
+    if slot.dtype not in _ELEM:
+        raise TypeError(f"unsupported element type {slot.dtype}")
+    _slot_size_ok(plan, slot, "slot")
+    flags = SMALL_FOOTPRINT if small else 0
+    _check(lib().tide_pack(plan.handle, tensors.array, ctypes.c_void_p(slot.data_ptr()),
+                           _ELEM[slot.dtype], flags, int(max_workgroups),
+                           _stream_handle(stream)))
+
+
+def slot_table(plan, slots):
+    """PointerTable for rs_slots: slots[r] = rank r's slot (N*S elements,
+    bf16, fp16 or fp32, one dtype for all), or one [N, N*S] tensor."""
+    if isinstance(slots, torch.Tensor):
+        if slots.dim() != 2 or slots.shape[0] != plan.world:
+            raise ValueError("a slot tensor must have shape [N, N*S]")
+        slots = list(slots)
+    if len(slots) != plan.world:
+        raise ValueError(f"expected {plan.world} slots, got {len(slots)}")
+    dtype = slots[0].dtype
+    if dtype not in _GRAD_FLAG:
+        raise TypeError(f"slots must be bfloat16, float16 or float32, got {dtype}")
+    for r, t in enumerate(slots):
+        if t.dtype != dtype:
+            raise TypeError(f"slots[{r}] is {t.dtype}, the others are {dtype}")
+        _slot_size_ok(plan, t, f"slots[{r}]")
+    return PointerTable(slots, dtype)
+
+
+def rs_slots(plan, rank, slots, out, small=False, max_workgroups=0, stream=None, avg=False):
+    """Stage 2 of the two-stage TIDE-RS: rank `rank`'s block from the N staged
+    slots (see slot_table), bit-identical to rs() over the gradients they
+    were packed from.  out, small, avg: as for rs()."""
+    if not isinstance(slots, PointerTable):
+        slots = slot_table(plan, slots)
+    if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_cuda \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 or bfloat16 device tensor")
+    if out.numel() != plan.S:
+        raise ValueError(f"out has {out.numel()} elements, expected S = {plan.S}")
+    flags = _GRAD_FLAG.get(slots.dtype, 0)
+    flags |= (SMALL_FOOTPRINT if small else 0) | (AVG if avg else 0)
+    flags |= OUT_BF16 if out.dtype == torch.bfloat16 else 0
+    _check(lib().tide_rs_slots(plan.handle, int(rank), slots.array,
+                               ctypes.c_void_p(out.data_ptr()), flags, int(max_workgroups),
+                               _stream_handle(stream)))
+
+
 __all__ = ["Plan", "PointerTable", "TideError", "SMALL_FOOTPRINT", "COPY_ENGINE", "AVG",
-           "GRAD_F16", "GRAD_F32", "grad_table",
-           "ag_tables",
-           "rs", "ag", "lib"]
+           "GRAD_F16", "GRAD_F32", "OUT_BF16", "grad_table",
+           "ag_tables", "slot_table",
+           "rs", "ag", "pack", "rs_slots", "lib"]

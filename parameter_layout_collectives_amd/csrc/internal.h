@@ -48,7 +48,9 @@ struct DeviceState {
     void *d_ag_tiles = nullptr;  // Tile[n_ag]
     void *d_ag_tiles_small = nullptr;  // Tile[n_ag_small]
     void *d_rs_tiles_small = nullptr;  // Tile[n_rs_small]
-    std::vector<PtrTable> rs_cache, ag_cache;
+    void *d_pack_tiles = nullptr;        // Tile[n_pack]
+    void *d_pack_tiles_small = nullptr;  // Tile[n_pack_small]
+    std::vector<PtrTable> rs_cache, ag_cache, pack_cache, slots_cache;
     uint64_t tick = 0;
 };
 
@@ -62,6 +64,7 @@ struct tide_plan {
     std::vector<int64_t> d0, inner, c, seg, off, numel;
     std::vector<tide::ParamDesc> desc;
     std::vector<tide::Tile> rs_tiles, rs_tiles_small, ag_tiles, ag_tiles_small;
+    std::vector<tide::Tile> pack_tiles, pack_tiles_small;
     mutable std::mutex mu;
     mutable std::vector<tide::DeviceState *> devs;
 };
@@ -90,6 +93,10 @@ tide_status check_rs_args(const tide_plan *p, int32_t rank, const void *const *g
 tide_status check_ag_args(const tide_plan *p, const void *const *rank_src,
                           void *const *params, int32_t elem_bytes, uint32_t flags,
                           int32_t max_wg);
+tide_status check_pack_args(const tide_plan *p, const void *const *tensors, const void *slot,
+                            int32_t elem_bytes, uint32_t flags, int32_t max_wg);
+tide_status check_rs_slots_args(const tide_plan *p, int32_t rank, const void *const *slots,
+                                const void *out, uint32_t flags, int32_t max_wg);
 
 // Frees the device tables of a plan (defined next to the kernels).
 void release_device_states(const tide_plan *p);

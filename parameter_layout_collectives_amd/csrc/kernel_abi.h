@@ -138,10 +138,26 @@ struct AgLaunch {
     hipStream_t stream;
 };
 
+// Everything one pack launch (stage 1 of the two-stage reduce-scatter)
+// needs.  ptrs: the P tensor pointers, then the slot pointer.  S: elements
+// per rank block of the slot.
+struct PackLaunch {
+    const ParamDesc *pd;
+    const Tile *tiles;
+    int64_t ntiles;
+    const uintptr_t *ptrs;
+    int P, elem_bytes;
+    int64_t S;
+    unsigned grid;
+    int lds;
+    hipStream_t stream;
+};
+
 // Enqueue one launch.  `small` selects the small-footprint tile list's
 // kernel shape (the caller passes that tile list).  Returns the HIP error of
 // the launch (or of allowing its LDS reservation).
 hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, bool small);
 hipError_t launch_ag(const AgLaunch &a, bool small);
+hipError_t launch_pack(const PackLaunch &a, bool small);
 
 }  // namespace tide

@@ -413,6 +413,59 @@ __global__ __launch_bounds__(BLOCK) void ag_kernel(const ParamDesc *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Pack kernel (stage 1 of the two-stage reduce-scatter)
+// ---------------------------------------------------------------------------
+//
+// The inverse placement of TIDE-AG: one rank's per-parameter tensors laid
+// out rank-major in a staging slot (for Slot-Reuse, the vacated all-gather
+// buffer).  Tile t covers elements [k0, k0 + TILE) of parameter i's span in
+// block q = tile.rank:
+//   k <  L(q,i):  slot[q*S + off_i + k] = tensors[i][q*seg_i + k]
+//   k >= L(q,i):  slot[q*S + off_i + k] = 0   (padding rows, alignment gap)
+// ptrs = tensors[0..P) followed by the slot.  The copy takes the widest
+// vector both addresses allow, as in ag_kernel.
+template <int BLOCK, int U, bool XMAP, int64_t TILE>
+__global__ __launch_bounds__(BLOCK) void pack_kernel(const ParamDesc *__restrict__ pdesc,
+                                                      const Tile *__restrict__ tiles,
+                                                      int64_t ntiles,
+                                                      const uintptr_t *__restrict__ ptrs, int P,
+                                                      int64_t S, int e) {
+    for (int64_t v = blockIdx.x; v < ntiles; v += gridDim.x) {
+        const Tile tile = tiles[XMAP ? xcd_tile(v, ntiles) : v];
+        const ParamDesc d = pdesc[tile.param];
+        const int64_t src = static_cast<int64_t>(tile.rank) * d.seg;
+        int64_t L = d.numel - src;
+        L = L < 0 ? 0 : (L > d.seg ? d.seg : L);
+        const int64_t kb = tile.k0;
+        const int64_t ke = min(kb + TILE, d.span);
+        char *blk = reinterpret_cast<char *>(ptrs[P]) +
+                    (static_cast<int64_t>(tile.rank) * S + d.off) * e;
+        const int64_t re = min(ke, L);
+        if (kb < re) {
+            const char *s = reinterpret_cast<const char *>(ptrs[tile.param]) + (src + kb) * e;
+            char *dst = blk + kb * e;
+            const int n = static_cast<int>((re - kb) * e);
+            const uintptr_t diff = reinterpret_cast<uintptr_t>(s) ^ reinterpret_cast<uintptr_t>(dst);
+            if ((diff & 15) == 0)
+                copy_span_w<BLOCK, 16, U>(s, dst, n, e);
+            else if ((diff & 7) == 0)
+                copy_span_w<BLOCK, 8, U>(s, dst, n, e);
+            else if ((diff & 3) == 0)
+                copy_span_w<BLOCK, 4, U>(s, dst, n, e);
+            else
+                copy_span_w<BLOCK, 2, U>(s, dst, n, e);
+        }
+        GLOBAL_AS char *z = gstore_ptr<char>(blk);
+        for (int64_t k = max(kb, L) + threadIdx.x; k < ke; k += BLOCK) {
+            if (e == 2)
+                *reinterpret_cast<GLOBAL_AS uint16_t *>(z + k * 2) = 0;
+            else
+                *reinterpret_cast<GLOBAL_AS uint32_t *>(z + k * 4) = 0;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch functions
 // ---------------------------------------------------------------------------
 
@@ -450,6 +503,17 @@ hipError_t launch_ag_t(const AgLaunch &a) {
     return hipGetLastError();
 }
 
+template <bool SMALL>
+hipError_t launch_pack_t(const PackLaunch &a) {
+    auto k = SMALL ? pack_kernel<TIDE_SMALL_BLOCK, TIDE_SMALL_AG_U, TIDE_XMAP_AG, kAgTileSmall>
+                   : pack_kernel<kBlock, kAgVecsPerLane, TIDE_XMAP_AG, kAgTile>;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(k), a.lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_BLOCK : kBlock), a.lds, a.stream,
+                       a.pd, a.tiles, a.ntiles, a.ptrs, a.P, a.S, a.elem_bytes);
+    return hipGetLastError();
+}
+
 template <int OT>
 hipError_t launch_rs_o(const RsLaunch &a, GradType type, bool small) {
     switch (type) {
@@ -470,6 +534,11 @@ hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, bool small) 
 hipError_t launch_ag(const AgLaunch &a, bool small) {
     (void)hipGetLastError();
     return small ? launch_ag_t<true>(a) : launch_ag_t<false>(a);
+}
+
+hipError_t launch_pack(const PackLaunch &a, bool small) {
+    (void)hipGetLastError();
+    return small ? launch_pack_t<true>(a) : launch_pack_t<false>(a);
 }
 
 }  // namespace tide

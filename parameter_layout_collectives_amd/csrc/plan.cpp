@@ -172,6 +172,82 @@ tide_status check_ag_args(const tide_plan *p, const void *const *rank_src,
     return TIDE_OK;
 }
 
+tide_status check_pack_args(const tide_plan *p, const void *const *tensors, const void *slot,
+                            int32_t elem_bytes, uint32_t flags, int32_t max_wg) {
+    if (!p) return fail(TIDE_E_INVALID, "tide_pack: plan is NULL");
+    if (elem_bytes != 2 && elem_bytes != 4)
+        return fail(TIDE_E_INVALID, "tide_pack: elem_bytes must be 2 or 4");
+    if (flags & ~TIDE_F_SMALL_FOOTPRINT)
+        return fail(TIDE_E_UNSUPPORTED, "tide_pack: unsupported flag bits");
+    if (max_wg < 0) return fail(TIDE_E_INVALID, "tide_pack: max_workgroups < 0");
+    if (p->S == 0) return TIDE_OK;
+    if (!tensors) return fail(TIDE_E_INVALID, "tide_pack: tensors array is NULL");
+    const uintptr_t e = static_cast<uintptr_t>(elem_bytes);
+    const uintptr_t d = reinterpret_cast<uintptr_t>(slot);
+    if (!d) return fail(TIDE_E_INVALID, "tide_pack: slot is NULL");
+    if (d % e) return fail(TIDE_E_INVALID, "tide_pack: slot is not aligned to its element size");
+    // The slot (N*S elements) is written whole; each tensor is read whole.
+    const Span written{d, d + static_cast<uintptr_t>(p->N) * static_cast<uintptr_t>(p->S) * e};
+    for (int32_t i = 0; i < p->P; i++) {
+        if (p->numel[i] == 0) continue;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(tensors[i]);
+        if (!a) return fail(TIDE_E_INVALID, "tide_pack: tensors[" + std::to_string(i) + "] is NULL");
+        if (a % e)
+            return fail(TIDE_E_INVALID, "tide_pack: tensors[" + std::to_string(i) +
+                                            "] is not aligned to its element size");
+        if (overlap(Span{a, a + static_cast<uintptr_t>(p->numel[i]) * e}, written))
+            return fail(TIDE_E_INVALID, "tide_pack: the slot overlaps tensors[" +
+                                            std::to_string(i) + "]");
+    }
+    return TIDE_OK;
+}
+
+tide_status check_rs_slots_args(const tide_plan *p, int32_t rank, const void *const *slots,
+                                const void *out, uint32_t flags, int32_t max_wg) {
+    if (!p) return fail(TIDE_E_INVALID, "tide_rs_slots: plan is NULL");
+    if (rank < 0 || rank >= p->N)
+        return fail(TIDE_E_INVALID, "tide_rs_slots: rank " + std::to_string(rank) +
+                                        " outside [0, " + std::to_string(p->N) + ")");
+    if (flags & TIDE_F_COPY_ENGINE)
+        return fail(TIDE_E_UNSUPPORTED, "tide_rs_slots: TIDE_F_COPY_ENGINE is for tide_ag");
+    if (flags & ~(TIDE_F_SMALL_FOOTPRINT | TIDE_F_AVG | TIDE_F_GRAD_F16 | TIDE_F_GRAD_F32 |
+                  TIDE_F_OUT_BF16))
+        return fail(TIDE_E_UNSUPPORTED, "tide_rs_slots: unknown flag bits");
+    if ((flags & TIDE_F_GRAD_F16) && (flags & TIDE_F_GRAD_F32))
+        return fail(TIDE_E_INVALID,
+                    "tide_rs_slots: TIDE_F_GRAD_F16 and TIDE_F_GRAD_F32 both set");
+    const uintptr_t es = (flags & TIDE_F_GRAD_F32) ? 4u : 2u;
+    const uintptr_t os = (flags & TIDE_F_OUT_BF16) ? 2u : 4u;
+    if (max_wg < 0) return fail(TIDE_E_INVALID, "tide_rs_slots: max_workgroups < 0");
+    if (p->S == 0) return TIDE_OK;
+    if (!slots) return fail(TIDE_E_INVALID, "tide_rs_slots: slots array is NULL");
+    if (!out) return fail(TIDE_E_INVALID, "tide_rs_slots: out is NULL");
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out);
+    if (o % os) return fail(TIDE_E_INVALID, "tide_rs_slots: out is not aligned to its element size");
+    const Span written{o, o + static_cast<uintptr_t>(p->S) * os};
+    for (int32_t r = 0; r < p->N; r++) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(slots[r]);
+        if (!a)
+            return fail(TIDE_E_INVALID, "tide_rs_slots: slots[" + std::to_string(r) + "] is NULL");
+        if (a % es)
+            return fail(TIDE_E_INVALID, "tide_rs_slots: slots[" + std::to_string(r) +
+                                            "] is not aligned to its element size");
+        // Block `rank` of slot r: the runs of real elements are read.
+        const uintptr_t blk = a + static_cast<uintptr_t>(rank) * static_cast<uintptr_t>(p->S) * es;
+        for (int32_t i = 0; i < p->P; i++) {
+            int64_t src, L;
+            shard_run(p, rank, i, &src, &L);
+            if (L == 0) continue;
+            const Span read{blk + static_cast<uintptr_t>(p->off[i]) * es,
+                            blk + static_cast<uintptr_t>(p->off[i] + L) * es};
+            if (overlap(read, written))
+                return fail(TIDE_E_INVALID,
+                            "tide_rs_slots: out overlaps slot elements it would read");
+        }
+    }
+    return TIDE_OK;
+}
+
 }  // namespace tide
 
 using tide::fail;
@@ -255,6 +331,15 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int64_t *dim0
                 for (int64_t k = 0; k < L; k += tide::kAgTile) p->ag_tiles.push_back({i, r, k});
                 for (int64_t k = 0; k < L; k += tide::kAgTileSmall)
                     p->ag_tiles_small.push_back({i, r, k});
+            }
+        // Pack tiles cover every position of every (param, rank) span of a
+        // staging slot: real elements are copied, padding and gaps zeroed.
+        for (int32_t i = 0; i < nparams; i++)
+            for (int32_t r = 0; r < world; r++) {
+                for (int64_t k = 0; k < p->desc[i].span; k += tide::kAgTile)
+                    p->pack_tiles.push_back({i, r, k});
+                for (int64_t k = 0; k < p->desc[i].span; k += tide::kAgTileSmall)
+                    p->pack_tiles_small.push_back({i, r, k});
             }
     } catch (const std::bad_alloc &) {
         delete p;

@@ -68,8 +68,10 @@ void free_state(DeviceState *ds) {
     (void)hipFree(ds->d_rs_tiles);
     (void)hipFree(ds->d_ag_tiles);
     (void)hipFree(ds->d_ag_tiles_small);
+    (void)hipFree(ds->d_pack_tiles);
+    (void)hipFree(ds->d_pack_tiles_small);
     (void)hipFree(ds->d_rs_tiles_small);
-    for (auto *cache : {&ds->rs_cache, &ds->ag_cache})
+    for (auto *cache : {&ds->rs_cache, &ds->ag_cache, &ds->pack_cache, &ds->slots_cache})
         for (auto &pt : *cache) {
             (void)hipFree(pt.dev);
             (void)hipHostFree(pt.staging);
@@ -138,6 +140,12 @@ tide_status device_state(const tide_plan *p, DeviceState **out) {
     if (st == TIDE_OK)
         st = upload(p->ag_tiles_small.data(), p->ag_tiles_small.size() * sizeof(Tile),
                     &ds->d_ag_tiles_small, "all-gather tiles (small footprint)");
+    if (st == TIDE_OK)
+        st = upload(p->pack_tiles.data(), p->pack_tiles.size() * sizeof(Tile), &ds->d_pack_tiles,
+                    "pack tiles");
+    if (st == TIDE_OK)
+        st = upload(p->pack_tiles_small.data(), p->pack_tiles_small.size() * sizeof(Tile),
+                    &ds->d_pack_tiles_small, "pack tiles (small footprint)");
     if (st != TIDE_OK) {
         free_state(ds);
         return st;
@@ -313,8 +321,9 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const P
     pt->upload_stream = static_cast<void *>(stream);
     pt->upload_done = false;
     pt->hash = h;
+    // Over the table as the kernel reads it (null padding entries are aligned).
     pt->aligned16 = true;
-    for (uintptr_t a : pt->key) pt->aligned16 = pt->aligned16 && (a & 15) == 0;
+    for (size_t j = 0; j < dev_len; j++) pt->aligned16 = pt->aligned16 && (staged[j] & 15) == 0;
     pt->last_use = ++ds->tick;
     *out = pt;
     return TIDE_OK;
@@ -523,6 +532,123 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
                            static_cast<hipStream_t>(stream)};
     hipError_t e = tide::launch_ag(L, small);
     if (e != hipSuccess) return tide::hip_fail("tide_ag: kernel launch", e);
+    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    if (st != TIDE_OK) return st;
+    tide::clear_error();
+    return TIDE_OK;
+}
+
+extern "C" tide_status tide_pack(const tide_plan *plan, const void *const *tensors, void *slot,
+                                 int32_t elem_bytes, uint32_t flags, int32_t max_workgroups,
+                                 void *stream) {
+    tide_status st =
+        tide::check_pack_args(plan, tensors, slot, elem_bytes, flags, max_workgroups);
+    if (st != TIDE_OK) return st;
+    if (plan->pack_tiles.empty()) return TIDE_OK;
+
+    // Table: the P tensor pointers, then the slot.
+    const uintptr_t slot_key[1] = {reinterpret_cast<uintptr_t>(slot)};
+    const tide::PtrKey key{reinterpret_cast<const uintptr_t *>(tensors),
+                           static_cast<size_t>(plan->P), slot_key, 1};
+    const size_t n = key.size();
+    const int32_t P = plan->P;
+    auto order = [P](const uintptr_t *k, uintptr_t *dev) {
+        std::copy(k, k + P + 1, dev);
+    };
+
+    std::lock_guard<std::mutex> lock(plan->mu);
+    tide::DeviceState *ds = nullptr;
+    st = tide::device_state(plan, &ds);
+    if (st != TIDE_OK) return st;
+    tide::PtrTable *pt = nullptr;
+    st = tide::pointer_table(ds, ds->pack_cache, key, n, order, static_cast<hipStream_t>(stream),
+                             &pt);
+    if (st != TIDE_OK) return st;
+
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    const int64_t ntiles =
+        static_cast<int64_t>(small ? plan->pack_tiles_small.size() : plan->pack_tiles.size());
+    const tide::PackLaunch L{static_cast<const tide::ParamDesc *>(ds->d_params),
+                             static_cast<const tide::Tile *>(small ? ds->d_pack_tiles_small
+                                                                   : ds->d_pack_tiles),
+                             ntiles,
+                             static_cast<const uintptr_t *>(pt->dev),
+                             plan->P,
+                             elem_bytes,
+                             plan->S,
+                             tide::grid_size(ds, ntiles, flags, max_workgroups),
+                             small ? ds->small_lds : ds->ag_cap_lds,
+                             static_cast<hipStream_t>(stream)};
+    hipError_t e = tide::launch_pack(L, small);
+    if (e != hipSuccess) return tide::hip_fail("tide_pack: kernel launch", e);
+    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    if (st != TIDE_OK) return st;
+    tide::clear_error();
+    return TIDE_OK;
+}
+
+extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
+                                     const void *const *slots, void *out, uint32_t flags,
+                                     int32_t max_workgroups, void *stream) {
+    tide_status st = tide::check_rs_slots_args(plan, rank, slots, out, flags, max_workgroups);
+    if (st != TIDE_OK) return st;
+    if (plan->S == 0) return TIDE_OK;
+
+    // The reduce-scatter kernel reads rank r's elements of parameter i at
+    // table[i*N + r] + (src(R,i) + k) * es.  Pointing that entry at
+    //   slots[r] + (R*S + off_i - src(R,i)) * es
+    // makes it read slot r's block R at off_i + k: the staged copy of the
+    // same element.  (R*S + off_i >= R*seg_i, so the entry stays inside the
+    // slot.)  The key holds the slot pointers, R and the element size.
+    const int32_t N = plan->N, P = plan->P;
+    const uintptr_t es = (flags & TIDE_F_GRAD_F32) ? 4u : 2u;
+    const uintptr_t extra[2] = {static_cast<uintptr_t>(rank), es};
+    const tide::PtrKey key{reinterpret_cast<const uintptr_t *>(slots), static_cast<size_t>(N),
+                           extra, 2};
+    const int64_t S = plan->S;
+    const std::vector<int64_t> &off = plan->off, &seg = plan->seg;
+    auto synth = [N, P, rank, es, S, &off, &seg](const uintptr_t *k, uintptr_t *dev) {
+        for (int32_t i = 0; i < P; i++) {
+            const int64_t rel = static_cast<int64_t>(rank) * S + off[i] -
+                                static_cast<int64_t>(rank) * seg[i];
+            for (int32_t r = 0; r < N; r++)
+                dev[static_cast<size_t>(i) * N + r] = k[r] + static_cast<uintptr_t>(rel) * es;
+        }
+    };
+
+    std::lock_guard<std::mutex> lock(plan->mu);
+    tide::DeviceState *ds = nullptr;
+    st = tide::device_state(plan, &ds);
+    if (st != TIDE_OK) return st;
+    tide::PtrTable *pt = nullptr;
+    st = tide::pointer_table(ds, ds->slots_cache, key,
+                             static_cast<size_t>(N) * P + tide::kPtrPad, synth,
+                             static_cast<hipStream_t>(stream), &pt);
+    if (st != TIDE_OK) return st;
+
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    const int64_t ntiles =
+        static_cast<int64_t>(small ? plan->rs_tiles_small.size() : plan->rs_tiles.size());
+    const tide::RsLaunch L{static_cast<const tide::ParamDesc *>(ds->d_params),
+                           static_cast<const tide::Tile *>(small ? ds->d_rs_tiles_small
+                                                                 : ds->d_rs_tiles),
+                           ntiles,
+                           static_cast<const char *const *>(pt->dev),
+                           N,
+                           rank,
+                           (flags & TIDE_F_AVG) ? 1 : 0,
+                           out,
+                           pt->aligned16 ? 1 : 0,
+                           (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
+                           tide::grid_size(ds, ntiles, flags, max_workgroups),
+                           small ? ds->small_lds : ds->rs_cap_lds,
+                           static_cast<hipStream_t>(stream)};
+    const tide::GradType type = (flags & TIDE_F_GRAD_F32)   ? tide::kF32
+                                : (flags & TIDE_F_GRAD_F16) ? tide::kF16
+                                                            : tide::kBf16;
+    const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
+    hipError_t e = tide::launch_rs(L, type, otype, small);
+    if (e != hipSuccess) return tide::hip_fail("tide_rs_slots: kernel launch", e);
     st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
     if (st != TIDE_OK) return st;
     tide::clear_error();

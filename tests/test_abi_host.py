@@ -194,6 +194,65 @@ def test_ag_empty_plan_is_a_noop():
     assert _ag(plan, None, None) == 0
 
 
+def _pack(plan, tensors, slot, e=2, flags=0, max_wg=0):
+    return lib().tide_pack(plan.handle if plan else None, tensors, ctypes.c_void_p(slot), e,
+                           flags, max_wg, None)
+
+
+def test_pack_argument_errors():
+    plan = tide.Plan([(4, 4), (8,)], 2)        # S = 12; tensor sizes 16, 8
+    ts = _ptrs([A, A + 0x1000])
+    slot = A + 0x10000
+    L = lib()
+    assert _pack(None, ts, slot) == E_INVALID
+    assert _pack(plan, ts, slot, e=8) == E_INVALID and b"elem_bytes" in L.tide_last_error()
+    assert _pack(plan, ts, slot, flags=0x2) == E_UNSUPPORTED
+    assert _pack(plan, ts, slot, flags=0x4) == E_UNSUPPORTED
+    assert _pack(plan, ts, slot, max_wg=-1) == E_INVALID
+    assert _pack(plan, None, slot) == E_INVALID
+    assert _pack(plan, ts, 0) == E_INVALID and b"slot is NULL" in L.tide_last_error()
+    assert _pack(plan, ts, slot + 1) == E_INVALID and b"aligned" in L.tide_last_error()
+    assert _pack(plan, ts, slot + 2, e=4) == E_INVALID
+    assert _pack(plan, _ptrs([A, None]), slot) == E_INVALID
+    assert _pack(plan, _ptrs([A + 1, A + 0x1000]), slot) == E_INVALID
+    # the slot (2*12 elements = 48 bytes) overlaps tensor 1 (bytes 0x1000..0x1010)
+    assert _pack(plan, ts, A + 0x1000 - 40) == E_INVALID
+    assert b"overlaps" in L.tide_last_error()
+
+
+def test_pack_empty_plan_is_a_noop():
+    plan = tide.Plan([(0, 3)], 4)
+    assert _pack(plan, None, 0) == 0
+
+
+def _rss(plan, rank, slots, out, flags=0, max_wg=0):
+    return lib().tide_rs_slots(plan.handle if plan else None, rank, slots, ctypes.c_void_p(out),
+                               flags, max_wg, None)
+
+
+def test_rs_slots_argument_errors():
+    plan = tide.Plan([(4, 4), (8,)], 2)        # S = 12; block 1 of a slot = bytes 24..48
+    slots = _ptrs([A, A + 0x1000])
+    out = A + 0x100000
+    L = lib()
+    assert _rss(None, 0, slots, out) == E_INVALID
+    assert _rss(plan, 2, slots, out) == E_INVALID and b"rank" in L.tide_last_error()
+    assert _rss(plan, 0, slots, out, flags=0x2) == E_UNSUPPORTED
+    assert _rss(plan, 0, slots, out, flags=0x40) == E_UNSUPPORTED
+    assert _rss(plan, 0, slots, out, flags=0x18) == E_INVALID
+    assert _rss(plan, 0, slots, out, max_wg=-1) == E_INVALID
+    assert _rss(plan, 0, None, out) == E_INVALID
+    assert _rss(plan, 0, slots, 0) == E_INVALID and b"out is NULL" in L.tide_last_error()
+    assert _rss(plan, 0, slots, out + 2) == E_INVALID and b"aligned" in L.tide_last_error()
+    assert _rss(plan, 0, slots, out + 1, flags=0x20) == E_INVALID
+    assert _rss(plan, 0, _ptrs([A, None]), out) == E_INVALID
+    assert _rss(plan, 0, _ptrs([A + 1, A + 0x1000]), out) == E_INVALID
+    assert _rss(plan, 0, _ptrs([A, A + 0x1002]), out, flags=0x10) == E_INVALID
+    # out overlaps the real elements of block 1 of slot 1 (read for rank 1)
+    assert _rss(plan, 1, slots, A + 0x1000 + 24) == E_INVALID
+    assert b"overlaps" in L.tide_last_error()
+
+
 def test_python_binding_rejects_bad_tensors():
     import torch
     plan = tide.Plan([(4, 4)], 2)
