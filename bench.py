@@ -223,6 +223,110 @@ def two_stage_leg(step, reps=16, warmup=2):
             "staging_bytes_per_rank": 2 * N * S, "staging_bytes_with_slot_reuse": 0}
 
 
+def _rmsnorm(x, w, eps=1e-5):
+    xf = x.float()
+    return (xf * torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)).to(x.dtype) * w
+
+
+def decoder_layer_fwd_bwd(p, x, n_heads, n_kv):
+    """Forward and backward of one Llama-shaped decoder layer on one
+    micro-batch x [T, D] with bf16 weights p = (q, k, v, o, gate, up, down,
+    norm1, norm2).  Every product is a 2-D GEMM: the attention core is an
+    elementwise stand-in (sigmoid(q * k) * v per head, k and v shared by
+    groups of heads) with the real parameters and gradient shapes, because
+    batched bf16 products can fault on these GPUs."""
+    q_w, k_w, v_w, o_w, g_w, u_w, d_w, n1, n2 = p
+    T = x.shape[0]
+    hd = q_w.shape[0] // n_heads
+    h = _rmsnorm(x, n1)
+    q = torch.nn.functional.linear(h, q_w).view(T, n_kv, n_heads // n_kv, hd)
+    k = torch.nn.functional.linear(h, k_w).view(T, n_kv, 1, hd)
+    v = torch.nn.functional.linear(h, v_w).view(T, n_kv, 1, hd)
+    a = (torch.sigmoid(q * k) * v).reshape(T, q_w.shape[0])
+    x1 = x + torch.nn.functional.linear(a, o_w)
+    h2 = _rmsnorm(x1, n2)
+    m = torch.nn.functional.silu(torch.nn.functional.linear(h2, g_w)) * \
+        torch.nn.functional.linear(h2, u_w)
+    y = x1 + torch.nn.functional.linear(m, d_w)
+    y.float().square().mean().backward()
+
+
+def layout_conversion_leg(step, tokens=8192, reps=3):
+    """One GPU's share of a data-parallel step of the workload's decoder layer
+    (8K tokens per GPU, as in the pages' 70B runs): forward and backward of
+    one micro-batch, then this rank's tide_rs and tide_ag.  Beside it, the
+    layout copies TIDE removes, timed as FSDP2 makes them with torch ops:
+    the gradient pack (per-parameter bf16 -> padded rank-major fp32 buffer)
+    and the all-gather copy-out (rank-major bf16 buffer -> per-parameter
+    tensors).  Their share of the step is the analogue of the pages' 6.4%."""
+    w, plan, N, S = step.w, step.plan, step.w.world, step.plan.S
+    if len(w.shapes) != 9:
+        return None                       # dense decoder layers only
+    D = w.shapes[0][1]
+    n_heads, n_kv = w.shapes[0][0] // 128, w.shapes[1][0] // 128
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    params = [(torch.randn(s, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+              .requires_grad_() for s in w.shapes]
+    x = torch.randn(tokens, D, generator=gen, device="cuda").to(torch.bfloat16)
+    segs = [(plan.param(i)[0], plan.param(i)[2]) for i in range(plan.P)]
+
+    def fwd_bwd():
+        for t in params:
+            t.grad = None
+        decoder_layer_fwd_bwd(params, x, n_heads, n_kv)
+
+    def stock_pack():
+        parts = []
+        for t, (off, seg) in zip(params, segs):
+            d0, inner = (t.shape[0], t.numel() // t.shape[0])
+            c = seg // inner
+            g = t.grad.view(d0, inner)
+            if N * c > d0:
+                g = torch.nn.functional.pad(g, (0, 0, 0, N * c - d0))
+            parts.append(g.reshape(N, seg))
+        return torch.cat(parts, dim=1).float()
+
+    def stock_copy_out():
+        gb = step.gathered.view(N, S)
+        for t, (off, seg) in zip(params, segs):
+            d0, inner = (t.shape[0], t.numel() // t.shape[0])
+            t.data.copy_(gb[:, off:off + seg].reshape(-1, inner)[:d0].view(t.shape))
+
+    fwd_bwd()
+    torch.cuda.synchronize()
+    assert all(t.grad is not None for t in params)
+    res = {}
+    for name, fn in (("fwd_bwd", fwd_bwd), ("stock_grad_pack", stock_pack),
+                     ("stock_copy_out", stock_copy_out),
+                     ("tide_rs", lambda: step.rs(0)), ("tide_ag", step.ag)):
+        fn()
+        ev = timed_events(reps)
+        torch.cuda.synchronize()
+        for k in range(reps):
+            ev[k][0].record()
+            fn()
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = statistics.median(a.elapsed_time(b) for a, b in ev)
+    copies = res["stock_grad_pack_ms"] + res["stock_copy_out_ms"]
+    stock_step = res["fwd_bwd_ms"] + copies
+    res.update({
+        "tokens": tokens,
+        "attention_core": "elementwise stand-in (no batched bf16 products)",
+        "stock_layout_copies_ms": copies,
+        "stock_layout_share_pct": 100.0 * copies / stock_step,
+        "tide_layout_copies_ms": 0.0,
+        "tide_local_collective_share_pct":
+            100.0 * (res["tide_rs_ms"] + res["tide_ag_ms"]) /
+            (res["fwd_bwd_ms"] + res["tide_rs_ms"] + res["tide_ag_ms"]),
+    })
+    log(f"layout conversion: fwd+bwd {res['fwd_bwd_ms']:.2f} ms, stock copies {copies:.2f} ms "
+        f"({res['stock_layout_share_pct']:.1f}% of the step), tide rs+ag "
+        f"{res['tide_rs_ms'] + res['tide_ag_ms']:.2f} ms")
+    del params, x
+    return res
+
+
 def kernel_stats(name, nbytes, times):
     mean = statistics.fmean(times)
     q = sorted(times)
@@ -528,6 +632,7 @@ def main():
 
     variants = None if args.no_variants else rs_variants(step)
     two_stage = None if args.no_variants else two_stage_leg(step)
+    layout = None if args.no_variants else layout_conversion_leg(step)
     copy_gbps = None if args.no_copy else copy_ceiling()
     if copy_gbps:
         log(f"copy ceiling {copy_gbps:.1f} GB/s")
@@ -580,6 +685,7 @@ def main():
         "tide_ag": ag_k,
         "tide_rs_variants": variants,
         "two_stage_rs": two_stage,
+        "layout_conversion": layout,
         "corun": corun_res,
         "corun_ag": corun_ag_res,
         "gemm_slowdown_pct": None if not corun_res else {

@@ -266,3 +266,15 @@ def test_python_binding_rejects_bad_tensors():
                                [torch.zeros(4, 4, dtype=torch.float16)]])
     with pytest.raises(ValueError):
         tide.grad_table(plan, cpu[:1])
+
+
+def test_custom_ops_registered():
+    """The PyTorch operators exist and declare the tensors they write."""
+    import torch
+    import parameter_layout_collectives_amd.torch_ops  # noqa: F401 - registers the ops
+    schemas = {n: str(getattr(torch.ops.tide, n).default._schema)
+               for n in ("rs", "ag", "pack", "rs_slots")}
+    assert "Tensor(a3!) out" in schemas["rs"]
+    assert "Tensor(a2!)[] params" in schemas["ag"]
+    assert "Tensor(a2!) slot" in schemas["pack"]
+    assert "Tensor(a3!) out" in schemas["rs_slots"]
