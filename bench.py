@@ -134,14 +134,23 @@ class Step:
         tide.ag(self.plan, None, None, small=self.small, tables=self.agt)
 
     def run(self, steps, warmup):
+        """Wall time of exactly `steps` back-to-back steps (synchronised on both
+        sides, nothing else on the stream), then the same steps again with a
+        HIP event pair around every launch for the per-kernel statistics."""
         N = self.w.world
         for k in range(warmup):
             self.rs(k % N)
             self.ag()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            self.rs(k % N)
+            self.ag()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
         ev_rs = timed_events(steps)
         ev_ag = timed_events(steps)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for k in range(steps):
             ev_rs[k][0].record()
             self.rs(k % N)
@@ -150,7 +159,6 @@ class Step:
             self.ag()
             ev_ag[k][1].record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         t_rs = [s.elapsed_time(e) * 1e-3 for s, e in ev_rs]
         t_ag = [s.elapsed_time(e) * 1e-3 for s, e in ev_ag]
         return wall, t_rs, t_ag

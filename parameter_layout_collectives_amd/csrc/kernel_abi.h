@@ -20,7 +20,7 @@ namespace tide {
 #define TIDE_AG_TILE 2048
 #endif
 #ifndef TIDE_AG_TILE_SMALL
-#define TIDE_AG_TILE_SMALL 16384
+#define TIDE_AG_TILE_SMALL 32768
 #endif
 #ifndef TIDE_RS_TILE_SMALL
 #define TIDE_RS_TILE_SMALL 2048
@@ -82,7 +82,13 @@ struct Tile {
 #define TIDE_XMAP_RS 0
 #endif
 #ifndef TIDE_SMALL_AG_U
-#define TIDE_SMALL_AG_U 8
+#define TIDE_SMALL_AG_U 4
+#endif
+// Small-footprint copies (all-gather placement, pack): one 1024-lane
+// workgroup per CU.  Its 16 light waves (few VGPRs, no ALU work) fit beside
+// a GEMM's resident waves and keep many bytes in flight.
+#ifndef TIDE_SMALL_AG_BLOCK
+#define TIDE_SMALL_AG_BLOCK 1024
 #endif
 #ifndef TIDE_XMAP_AG
 #define TIDE_XMAP_AG 1

@@ -493,24 +493,24 @@ hipError_t launch_rs_t(const RsLaunch &a) {
 
 template <bool SMALL>
 hipError_t launch_ag_t(const AgLaunch &a) {
-    auto k = SMALL ? ag_kernel<TIDE_SMALL_BLOCK, TIDE_SMALL_AG_U, TIDE_SMALL_PACE, TIDE_XMAP_AG,
+    auto k = SMALL ? ag_kernel<TIDE_SMALL_AG_BLOCK, TIDE_SMALL_AG_U, TIDE_SMALL_PACE, TIDE_XMAP_AG,
                                kAgTileSmall>
                    : ag_kernel<kBlock, kAgVecsPerLane, 0, TIDE_XMAP_AG, kAgTile>;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(k), a.lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_BLOCK : kBlock), a.lds, a.stream,
-                       a.pd, a.tiles, a.ntiles, a.ptrs, a.N, a.elem_bytes);
+    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_AG_BLOCK : kBlock), a.lds,
+                       a.stream, a.pd, a.tiles, a.ntiles, a.ptrs, a.N, a.elem_bytes);
     return hipGetLastError();
 }
 
 template <bool SMALL>
 hipError_t launch_pack_t(const PackLaunch &a) {
-    auto k = SMALL ? pack_kernel<TIDE_SMALL_BLOCK, TIDE_SMALL_AG_U, TIDE_XMAP_AG, kAgTileSmall>
+    auto k = SMALL ? pack_kernel<TIDE_SMALL_AG_BLOCK, TIDE_SMALL_AG_U, TIDE_XMAP_AG, kAgTileSmall>
                    : pack_kernel<kBlock, kAgVecsPerLane, TIDE_XMAP_AG, kAgTile>;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(k), a.lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_BLOCK : kBlock), a.lds, a.stream,
-                       a.pd, a.tiles, a.ntiles, a.ptrs, a.P, a.S, a.elem_bytes);
+    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_AG_BLOCK : kBlock), a.lds,
+                       a.stream, a.pd, a.tiles, a.ntiles, a.ptrs, a.P, a.S, a.elem_bytes);
     return hipGetLastError();
 }
 
