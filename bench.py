@@ -600,7 +600,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: runs on one GPU only (--gpus {args.gpus} requested); "
               "the N emulated ranks of the workload live in that GPU's memory.",
               file=sys.stderr, flush=True)
         sys.exit(2)
