@@ -1,7 +1,8 @@
 // Runtime of the TIDE library on the HIP side: per-device tables, the
 // pointer-table cache, the launch policy and the extern "C" entry points
-// tide_rs / tide_ag.  The kernels and their launch functions are in
-// kernels.hip; the host-only plan and argument checks in plan.cpp.
+// tide_rs, tide_ag, tide_pack and tide_rs_slots.  The kernels and their
+// launch functions are in kernels.hip; the host-only plan and argument
+// checks in plan.cpp.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
