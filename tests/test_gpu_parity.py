@@ -601,3 +601,43 @@ def test_table_upload_ordered_across_streams(orc):
     for out in (out_a, out_b):
         got = out.cpu().numpy()
         assert same_f32(got, want), first_mismatch(got, want)
+
+
+def test_table_slots_under_concurrent_eviction(orc):
+    """Two host threads, each with its own stream, cycle through 12 pointer
+    sets (more than the 8 cached slots), so slots are replaced while the
+    other stream may still read them: every result still equals the oracle."""
+    import threading
+    shapes = [(33, 5), (4100,)]
+    N = 3
+    plan = tide.Plan(shapes, N)
+    sets = [to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=3000 + 10 * j))
+            for j in range(12)]
+    outs = [[fresh_out(plan.S) for _ in range(len(sets))] for _ in range(2)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            for sweep in range(3):
+                for j in range(len(sets)):
+                    jj = (j * (t + 1) + sweep) % len(sets)
+                    tide.rs(plan, jj % N, sets[jj], outs[t][jj], stream=s)
+            s.synchronize()
+        except Exception as exc:  # noqa: BLE001 - reported below
+            errors.append(exc)
+
+    note("pointer-table slots: two streams, 12 sets, 8 slots")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for j, g in enumerate(sets):
+        want = expected_rs(orc, shapes, N, j % N, g, plan)
+        for t in range(2):
+            got = outs[t][j].cpu().numpy()
+            assert same_f32(got, want), (t, j, first_mismatch(got, want))
