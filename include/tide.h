@@ -54,6 +54,16 @@
  * Replacing a set waits (on the host) until the launches that read it have
  * finished.  A call on another stream that hits a set whose upload may still
  * be in flight makes its stream wait for that upload.
+ *
+ * Graph capture.  tide_rs, tide_ag, tide_pack and tide_rs_slots may be
+ * captured into a HIP graph (stream capture) once the plan has been used on
+ * the device and the call's pointer set is cached and uploaded: make the
+ * same call once outside the capture and synchronize first.  Otherwise the
+ * call returns TIDE_E_UNSUPPORTED and enqueues nothing.  A pointer set read
+ * by a captured launch keeps its cache slot for the plan's lifetime (the
+ * graph reads that slot at every replay); once all 8 slots of an operation
+ * are held that way, calls with a new pointer set return TIDE_E_UNSUPPORTED.
+ * Destroy the graphs before the plan.
  */
 #ifndef TIDE_H
 #define TIDE_H

@@ -31,6 +31,7 @@ struct PtrTable {
     void *uploaded = nullptr;    // hipEvent_t recorded after the upload of the current set
     void *upload_stream = nullptr;
     bool upload_done = false;    // the upload is known to have finished
+    bool pinned = false;         // read by a captured graph: never replaced
     bool aligned16 = false;      // every non-null pointer is 16-byte aligned
     uint64_t last_use = 0;
 };

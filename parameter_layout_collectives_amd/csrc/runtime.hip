@@ -89,9 +89,10 @@ int lds_for_cap(const DeviceState *ds, int cap) {
     return (want > 0 && want <= ds->lds_per_wg_max) ? want : 0;
 }
 
-// The plan's tables on the current device (created on first use).
+// The plan's tables on the current device (created on first use, which
+// allocates and copies synchronously, so never inside a graph capture).
 // Caller holds p->mu.
-tide_status device_state(const tide_plan *p, DeviceState **out) {
+tide_status device_state(const tide_plan *p, bool capturing, DeviceState **out) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
@@ -100,6 +101,10 @@ tide_status device_state(const tide_plan *p, DeviceState **out) {
             *out = ds;
             return TIDE_OK;
         }
+    if (capturing)
+        return fail(TIDE_E_UNSUPPORTED,
+                    "the first call of a plan on a device cannot be captured into a graph: "
+                    "make one call outside the capture first");
     DeviceState *ds = new (std::nothrow) DeviceState;
     if (!ds) return fail(TIDE_E_NOMEM, "device state: out of host memory");
     ds->device = dev;
@@ -198,10 +203,24 @@ tide_status mark_read(PtrTable *pt, hipStream_t stream) {
     return TIDE_OK;
 }
 
+// OK once the slot's upload has finished (checked without waiting);
+// TIDE_E_UNSUPPORTED while it is still in flight.
+tide_status upload_finished(PtrTable *pt) {
+    if (pt->upload_done) return TIDE_OK;
+    hipError_t e = hipEventQuery(static_cast<hipEvent_t>(pt->uploaded));
+    if (e == hipSuccess) {
+        pt->upload_done = true;
+        return TIDE_OK;
+    }
+    if (e != hipErrorNotReady) return hip_fail("pointer table: hipEventQuery", e);
+    return fail(TIDE_E_UNSUPPORTED,
+                "the pointer table is still being uploaded: synchronize before capturing");
+}
+
 // A launch on `stream` that reads the slot must not start before the upload
 // (enqueued on another stream, perhaps) has finished.
 tide_status order_after_upload(PtrTable *pt, hipStream_t stream) {
-    if (pt->upload_done || pt->upload_stream == static_cast<void *>(stream)) return TIDE_OK;
+    if (pt->upload_done) return TIDE_OK;
     const hipEvent_t up = static_cast<hipEvent_t>(pt->uploaded);
     hipError_t e = hipEventQuery(up);
     if (e == hipSuccess) {
@@ -209,6 +228,7 @@ tide_status order_after_upload(PtrTable *pt, hipStream_t stream) {
         return TIDE_OK;
     }
     if (e != hipErrorNotReady) return hip_fail("pointer table: hipEventQuery", e);
+    if (pt->upload_stream == static_cast<void *>(stream)) return TIDE_OK;   // stream order
     e = hipStreamWaitEvent(stream, up, 0);
     if (e != hipSuccess) return hip_fail("pointer table: hipStreamWaitEvent", e);
     return TIDE_OK;
@@ -254,16 +274,29 @@ tide_status drain_slot(PtrTable *pt) {
 // mark_read().  Caller holds p->mu.
 template <typename Order>
 tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const PtrKey &key,
-                          size_t dev_len, Order order, hipStream_t stream, PtrTable **out) {
+                          size_t dev_len, Order order, hipStream_t stream, bool capturing,
+                          PtrTable **out) {
     const uint64_t h = hash_ptrs(hash_ptrs(1469598103934665603ull, key.a, key.na), key.b, key.nb);
     for (auto &pt : cache)
         if (pt.hash == h && key.equals(pt.key)) {
-            tide_status st = order_after_upload(&pt, stream);
-            if (st != TIDE_OK) return st;
+            if (capturing) {
+                // A graph's launches read this slot at every replay: the
+                // upload must be complete now, and the slot is never reused.
+                tide_status st = upload_finished(&pt);
+                if (st != TIDE_OK) return st;
+                pt.pinned = true;
+            } else {
+                tide_status st = order_after_upload(&pt, stream);
+                if (st != TIDE_OK) return st;
+            }
             pt.last_use = ++ds->tick;
             *out = &pt;
             return TIDE_OK;
         }
+    if (capturing)
+        return fail(TIDE_E_UNSUPPORTED,
+                    "a pointer set the plan has not cached cannot be uploaded inside a graph "
+                    "capture: make one call with the same pointers outside the capture first");
     const size_t bytes = dev_len * sizeof(uintptr_t);
     PtrTable *pt = nullptr;
     if (cache.size() < kPtrCacheEntries) {
@@ -282,10 +315,12 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const P
         }
         pt = &cache.back();
     } else {
-        pt = &*std::min_element(cache.begin(), cache.end(),
-                                [](const PtrTable &a, const PtrTable &b) {
-                                    return a.last_use < b.last_use;
-                                });
+        pt = nullptr;
+        for (auto &c : cache)
+            if (!c.pinned && (!pt || c.last_use < pt->last_use)) pt = &c;
+        if (!pt)
+            return fail(TIDE_E_UNSUPPORTED,
+                        "every cached pointer set of this plan is read by a captured graph");
         tide_status drained = drain_slot(pt);
         if (drained != TIDE_OK) return drained;
     }
@@ -351,6 +386,21 @@ unsigned grid_size(const DeviceState *ds, int64_t ntiles, uint32_t flags, int32_
     return static_cast<unsigned>(std::max<int64_t>(g, 1));
 }
 
+// Whether work enqueued on `stream` is being captured into a graph.
+tide_status capture_status(void *stream, bool *capturing) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs);
+    if (e != hipSuccess) return hip_fail("hipStreamIsCapturing", e);
+    *capturing = cs == hipStreamCaptureStatusActive;
+    return TIDE_OK;
+}
+
+// After a launch: the slot's reader tracking (not while capturing - a
+// captured launch reads a pinned slot).
+tide_status after_launch(PtrTable *pt, hipStream_t stream, bool capturing) {
+    return capturing ? TIDE_OK : mark_read(pt, stream);
+}
+
 }  // namespace
 
 void release_device_states(const tide_plan *p) {
@@ -387,13 +437,16 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
                 dev[static_cast<size_t>(i) * N + r] = k[static_cast<size_t>(r) * P + i];
     };
 
+    bool capturing = false;
+    st = tide::capture_status(stream, &capturing);
+    if (st != TIDE_OK) return st;
     std::lock_guard<std::mutex> lock(plan->mu);
     tide::DeviceState *ds = nullptr;
-    st = tide::device_state(plan, &ds);
+    st = tide::device_state(plan, capturing, &ds);
     if (st != TIDE_OK) return st;
     tide::PtrTable *pt = nullptr;
     st = tide::pointer_table(ds, ds->rs_cache, key, key.size() + tide::kPtrPad, param_major,
-                             static_cast<hipStream_t>(stream), &pt);
+                             static_cast<hipStream_t>(stream), capturing, &pt);
     if (st != TIDE_OK) return st;
 
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
@@ -419,7 +472,7 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
     const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
     hipError_t e = tide::launch_rs(L, type, otype, small);
     if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
-    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;
     tide::clear_error();
     return TIDE_OK;
@@ -509,13 +562,16 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
     const size_t n = key.size();
     auto as_is = [n](const uintptr_t *k, uintptr_t *dev) { std::copy(k, k + n, dev); };
 
+    bool capturing = false;
+    st = tide::capture_status(stream, &capturing);
+    if (st != TIDE_OK) return st;
     std::lock_guard<std::mutex> lock(plan->mu);
     tide::DeviceState *ds = nullptr;
-    st = tide::device_state(plan, &ds);
+    st = tide::device_state(plan, capturing, &ds);
     if (st != TIDE_OK) return st;
     tide::PtrTable *pt = nullptr;
     st = tide::pointer_table(ds, ds->ag_cache, key, n, as_is, static_cast<hipStream_t>(stream),
-                             &pt);
+                             capturing, &pt);
     if (st != TIDE_OK) return st;
 
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
@@ -533,7 +589,7 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
                            static_cast<hipStream_t>(stream)};
     hipError_t e = tide::launch_ag(L, small);
     if (e != hipSuccess) return tide::hip_fail("tide_ag: kernel launch", e);
-    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;
     tide::clear_error();
     return TIDE_OK;
@@ -557,13 +613,16 @@ extern "C" tide_status tide_pack(const tide_plan *plan, const void *const *tenso
         std::copy(k, k + P + 1, dev);
     };
 
+    bool capturing = false;
+    st = tide::capture_status(stream, &capturing);
+    if (st != TIDE_OK) return st;
     std::lock_guard<std::mutex> lock(plan->mu);
     tide::DeviceState *ds = nullptr;
-    st = tide::device_state(plan, &ds);
+    st = tide::device_state(plan, capturing, &ds);
     if (st != TIDE_OK) return st;
     tide::PtrTable *pt = nullptr;
     st = tide::pointer_table(ds, ds->pack_cache, key, n, order, static_cast<hipStream_t>(stream),
-                             &pt);
+                             capturing, &pt);
     if (st != TIDE_OK) return st;
 
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
@@ -582,7 +641,7 @@ extern "C" tide_status tide_pack(const tide_plan *plan, const void *const *tenso
                              static_cast<hipStream_t>(stream)};
     hipError_t e = tide::launch_pack(L, small);
     if (e != hipSuccess) return tide::hip_fail("tide_pack: kernel launch", e);
-    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;
     tide::clear_error();
     return TIDE_OK;
@@ -617,14 +676,17 @@ extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
         }
     };
 
+    bool capturing = false;
+    st = tide::capture_status(stream, &capturing);
+    if (st != TIDE_OK) return st;
     std::lock_guard<std::mutex> lock(plan->mu);
     tide::DeviceState *ds = nullptr;
-    st = tide::device_state(plan, &ds);
+    st = tide::device_state(plan, capturing, &ds);
     if (st != TIDE_OK) return st;
     tide::PtrTable *pt = nullptr;
     st = tide::pointer_table(ds, ds->slots_cache, key,
                              static_cast<size_t>(N) * P + tide::kPtrPad, synth,
-                             static_cast<hipStream_t>(stream), &pt);
+                             static_cast<hipStream_t>(stream), capturing, &pt);
     if (st != TIDE_OK) return st;
 
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
@@ -650,7 +712,7 @@ extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
     const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
     hipError_t e = tide::launch_rs(L, type, otype, small);
     if (e != hipSuccess) return tide::hip_fail("tide_rs_slots: kernel launch", e);
-    st = tide::mark_read(pt, static_cast<hipStream_t>(stream));
+    st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;
     tide::clear_error();
     return TIDE_OK;
