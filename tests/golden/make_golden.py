@@ -1,8 +1,9 @@
 """Write tests/golden/tiny_expected.json from the CPU oracle.
 
 The stored values are the tiny workload's seeded bf16 gradients (bit
-patterns) and the oracle's fp32 reduce-scatter block for every rank (bit
-patterns).  Only the oracle and the seeded input generator are used; nothing
+patterns) and, for every rank, the oracle's fp32 reduce-scatter block (sum
+and mean), the sum rounded to bf16, and the rank-major pack of that rank's
+gradients (all as bit patterns).  Only the oracle and the seeded input generator are used; nothing
 here touches the HIP library.
 
     python tests/golden/make_golden.py
@@ -26,14 +27,20 @@ def main():
     grads = workloads.all_grads(w)
     bits = [[workloads.bf16_bits(t).reshape(-1) for t in rank] for rank in grads]
     orc = oracle.default()
-    rs = [orc.rs(w.shapes, w.world, R, bits).view(np.uint32).tolist() for R in range(w.world)]
+    rs = [orc.rs(w.shapes, w.world, R, bits) for R in range(w.world)]
+    mean = [orc.rs(w.shapes, w.world, R, bits, avg=True) for R in range(w.world)]
     doc = {
         "_about": "tiny workload: 3 params [5,7],[16],[33,4], 4 ranks, bf16 ~N(0,1), "
-                  "rank r seeded 0+r on a CPU generator; rs[R] = oracle fp32 block bits",
+                  "rank r seeded 0+r on a CPU generator; rs[R] = oracle fp32 block bits; "
+                  "rs_mean[R] = the mean's block; rs_bf16[R] = the sum's block rounded to "
+                  "bf16 (bits); pack[r] = rank r's gradients packed rank-major (bits)",
         "shapes": [list(s) for s in w.shapes],
         "world": w.world,
         "grads": [[b.tolist() for b in rank] for rank in bits],
-        "rs": rs,
+        "rs": [b.view(np.uint32).tolist() for b in rs],
+        "rs_mean": [b.view(np.uint32).tolist() for b in mean],
+        "rs_bf16": [orc.round_bf16(b).tolist() for b in rs],
+        "pack": [orc.pack(w.shapes, w.world, bits[r]).tolist() for r in range(w.world)],
     }
     with open(os.path.join(HERE, "tiny_expected.json"), "w") as f:
         json.dump(doc, f)

@@ -646,3 +646,7 @@ def test_tiny_golden(orc):
     for R in range(TINY.world):
         out = orc.rs(TINY.shapes, TINY.world, R, gb)
         assert bits_f32(out).tolist() == gold["rs"][R]
+        mean = orc.rs(TINY.shapes, TINY.world, R, gb, avg=True)
+        assert bits_f32(mean).tolist() == gold["rs_mean"][R]
+        assert orc.round_bf16(out).tolist() == gold["rs_bf16"][R]
+        assert orc.pack(TINY.shapes, TINY.world, gb[R]).tolist() == gold["pack"][R]
