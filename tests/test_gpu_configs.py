@@ -6,7 +6,8 @@ Workloads (architecture shapes only, synthetic seeded bf16 gradients):
   * Llama-3.1-70B-shaped decoder layer, 8 ranks;
   * Qwen3-30B-A3B-shaped MoE layer (391 parameters, 6256 gradient
     pointers), 16 ranks, 10% of experts all-zero per rank;
-  * Llama-3.1-70B-shaped layer at 64 ranks (~110 GB of gradients in HBM).
+  * Llama-3.1-70B-shaped layer at 64 ranks (~110 GB of gradients in HBM),
+    also with bf16 8192^3 GEMMs running on another stream (the co-run).
 
 The whole fp32 output block of each checked rank is compared bit for bit
 with the oracle, which reads host copies of exactly the gradient slices the
@@ -113,5 +114,31 @@ def test_llama70b_layer_64_ranks(orc):
     table = tide.grad_table(plan, grads)
     _rs_cases(orc, w, grads, plan, table, (0, 63), (False,))
     _rs_cases(orc, w, grads, plan, table, (1,), (True,))
-    del grads, table
+    # the co-run configuration: tide_rs on one stream while bf16 8192^3
+    # GEMMs run on another (the bench's co-run), results checked
+    M, K, Nn = w.corun_gemm
+    a = torch.randn(M, K, device=DEV).to(torch.bfloat16)
+    b = torch.randn(K, Nn, device=DEV).to(torch.bfloat16)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = {R: torch.empty(plan.S, dtype=torch.float32, device=DEV) for R in (5, 40)}
+    wants = {R: expected_rs(orc, w.shapes, w.world, R, grads, plan) for R in outs}
+    torch.cuda.synchronize()
+    note(f"{w.name}: tide_rs beside bf16 GEMMs")
+    with torch.cuda.stream(sa):
+        for _ in range(12):
+            torch.matmul(a, b)
+    for small in (True, False):
+        for R, o in outs.items():
+            o.view(torch.int32).fill_(F32_SENTINEL)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sa):
+            for _ in range(12):
+                torch.matmul(a, b)
+        for R, o in outs.items():
+            tide.rs(plan, R, table, o, small=small, stream=sb)
+        torch.cuda.synchronize()
+        for R, o in outs.items():
+            got = o.cpu().numpy()
+            assert same_f32(got, wants[R]), (R, small, first_mismatch(got, wants[R]))
+    del grads, table, a, b, outs
     _free()
