@@ -164,6 +164,31 @@ class Step:
         return wall, t_rs, t_ag
 
 
+def small_footprint_alone(step, reps=20, warmup=3):
+    """Event-timed small-footprint launches with nothing beside them, R
+    rotating (median, p10, p90 as for the default launch)."""
+    plan, N = step.plan, step.w.world
+    res = {}
+    for name, fn, nbytes in (
+            ("tide_rs", lambda k: tide.rs(plan, k % N, step.table, step.blocks[k % N], small=True),
+             step.b_rs),
+            ("tide_ag", lambda k: tide.ag(plan, None, None, small=True, tables=step.agt),
+             step.b_ag)):
+        for k in range(warmup):
+            fn(k)
+        ev = timed_events(reps)
+        torch.cuda.synchronize()
+        for k in range(reps):
+            ev[k][0].record()
+            fn(k)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        res[name] = kernel_stats(f"{name} (small footprint)", nbytes,
+                                 [a.elapsed_time(b) * 1e-3 for a, b in ev])
+        log(f"{name} small footprint alone: {res[name]['GBps']:.1f} GB/s")
+    return res
+
+
 def rs_variants(step, reps=20, warmup=3):
     """Event-timed tide_rs launches of the flag variants on the step's
     workload, R rotating: the bf16 shard (fp32 sum rounded once; half the
@@ -559,6 +584,22 @@ def cpu_baseline(step, min_reps=3, max_reps=40, budget_s=10.0):
         if k < 3:
             log(f"cpu baseline rep {k}: rs {t1 - t0:.3f} s, ag {t2 - t1:.3f} s")
     trs, tag = statistics.median(t_rs), statistics.median(t_ag)
+    # the tiny workload on one thread (latency, not bandwidth)
+    tw = workloads.WORKLOADS["tiny"]
+    tg = [[workloads.bf16_bits(t).reshape(-1) for t in rank] for rank in workloads.all_grads(tw)]
+    tplan = orc.geometry(tw.shapes, tw.world)
+    tblocks = [np.zeros(tplan.S, np.uint16) for _ in range(tw.world)]
+    threads = orc.threads()
+    orc.set_threads(1)
+    try:
+        t_tiny = []
+        for _ in range(200):
+            t0 = time.perf_counter()
+            orc.rs(tw.shapes, tw.world, 1, tg)
+            orc.ag(tw.shapes, tw.world, tblocks, elem_bytes=2)
+            t_tiny.append(time.perf_counter() - t0)
+    finally:
+        orc.set_threads(threads)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -577,6 +618,7 @@ def cpu_baseline(step, min_reps=3, max_reps=40, budget_s=10.0):
                    f"median of {len(t_rs)} repetitions (~{budget_s:.0f} s); host copies not timed"),
         "rs_s": trs,
         "ag_s": tag,
+        "tiny_step_us_1_thread": statistics.median(t_tiny) * 1e6,
         "cpu_model": cpu,
     }
 
@@ -639,6 +681,7 @@ def main():
     }
 
     variants = None if args.no_variants else rs_variants(step)
+    small_alone = None if args.no_variants else small_footprint_alone(step)
     two_stage = None if args.no_variants else two_stage_leg(step)
     layout = None if args.no_variants else layout_conversion_leg(step)
     copy_gbps = None if args.no_copy else copy_ceiling()
@@ -692,6 +735,7 @@ def main():
         "tide_rs": rs_k,
         "tide_ag": ag_k,
         "tide_rs_variants": variants,
+        "small_footprint_alone": small_alone,
         "two_stage_rs": two_stage,
         "layout_conversion": layout,
         "corun": corun_res,
