@@ -85,24 +85,37 @@ def timed_events(n):
             for _ in range(n)]
 
 
-def copy_ceiling(nbytes=2 << 30, reps=10):
-    """Device-to-device copy of nbytes (read + write) as the measured
-    ceiling next to the 8 TB/s spec."""
+def copy_ceiling(nbytes=2 << 30, reps=10, library=True):
+    """Device-to-device copies of nbytes (read + write) as measured ceilings
+    next to the 8 TB/s spec: torch's copy, and this library's own 16-byte
+    vector copy (tide_ag with one rank and one parameter: the rank block is
+    the whole tensor).  Returns (torch GB/s, library GB/s)."""
     n = nbytes // 2
     a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1.0)
-    for _ in range(3):
-        b.copy_(a)
-    ev = timed_events(reps)
-    for s, e in ev:
-        s.record()
-        b.copy_(a)
-        e.record()
-    torch.cuda.synchronize()
-    t = statistics.median(s.elapsed_time(e) for s, e in ev) * 1e-3
-    del a, b
-    return 2 * nbytes / t / 1e9
+    plan = tide.Plan([(n,)], 1)
+    tables = tide.ag_tables(plan, a, [b])
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = timed_events(reps)
+        for s, e in ev:
+            s.record()
+            fn()
+            e.record()
+        torch.cuda.synchronize()
+        return 2 * nbytes / (statistics.median(s.elapsed_time(e) for s, e in ev) * 1e-3) / 1e9
+
+    g_torch = timed(lambda: b.copy_(a))
+    g_lib = None
+    if library:
+        b.zero_()
+        g_lib = timed(lambda: tide.ag(plan, None, None, tables=tables))
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    del a, b, tables
+    return g_torch, g_lib
 
 
 # ---------------------------------------------------------------------------
@@ -636,6 +649,9 @@ def main():
                     help="workload for the co-run GEMM measurement, or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
+    ap.add_argument("--no-lib-copy", action="store_true",
+                    help="measure the copy ceiling with torch's copy only (profiled runs: the "
+                         "library's copy is an all-gather launch)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the tide_rs flag variants (bf16 shard, mean) and the "
                          "two-stage reduce-scatter")
@@ -684,9 +700,10 @@ def main():
     small_alone = None if args.no_variants else small_footprint_alone(step)
     two_stage = None if args.no_variants else two_stage_leg(step)
     layout = None if args.no_variants else layout_conversion_leg(step)
-    copy_gbps = None if args.no_copy else copy_ceiling()
+    copy_gbps, copy_lib_gbps = (None, None) if args.no_copy else \
+        copy_ceiling(library=not args.no_lib_copy)
     if copy_gbps:
-        log(f"copy ceiling {copy_gbps:.1f} GB/s")
+        log(f"copy ceiling {copy_gbps:.1f} GB/s (torch), {fmt(copy_lib_gbps)} GB/s (library)")
     cpu = None if args.no_cpu else cpu_baseline(step)
     corun_res = corun_ag_res = None
     gemm = None
@@ -732,6 +749,7 @@ def main():
         "pct_of_peak": 100.0 * value / HBM_PEAK_GBPS,
         "pct_of_copy_ceiling": None if not copy_gbps else 100.0 * value / copy_gbps,
         "copy_ceiling_GBps": copy_gbps,
+        "copy_ceiling_library_GBps": copy_lib_gbps,
         "tide_rs": rs_k,
         "tide_ag": ag_k,
         "tide_rs_variants": variants,
