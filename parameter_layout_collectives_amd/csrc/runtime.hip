@@ -39,6 +39,16 @@ namespace {
 #ifndef TIDE_SMALL_WG
 #define TIDE_SMALL_WG 32
 #endif
+// Small-footprint TIDE-RS for at most this many ranks runs the default
+// kernel shape (4 chunks per lane over 4096-element tiles) under the
+// small-footprint LDS reservation; for more ranks, the lighter small shape
+// (2 chunks per lane, 2048-element tiles, 16-rank batches).  Beside a bf16
+// 8192^3 GEMM the default shape moved 37% (8 ranks) and 20% (16 ranks)
+// more bytes than the small one at 0.3% and 3.5% GEMM slowdown, but at 64
+// ranks it cost the GEMM 9.9% against the small shape's 4.6-7.1%.
+#ifndef TIDE_SMALL_FEW_RANKS
+#define TIDE_SMALL_FEW_RANKS 16
+#endif
 constexpr int kWgPerCu = TIDE_WG_PER_CU;      // default grid: enough waves to keep HBM busy
 constexpr int kSmallFootprintWg = TIDE_SMALL_WG;  // small-footprint grid
 
@@ -386,6 +396,25 @@ unsigned grid_size(const DeviceState *ds, int64_t ntiles, uint32_t flags, int32_
     return static_cast<unsigned>(std::max<int64_t>(g, 1));
 }
 
+// The reduce-scatter launch for `flags`: kernel shape, tile list, LDS.
+struct RsShape {
+    bool small_kernel;   // the small-footprint kernel shape and its tile list
+    const Tile *tiles;
+    int64_t ntiles;
+    int lds;
+};
+
+RsShape rs_shape(const tide_plan *p, const DeviceState *ds, uint32_t flags) {
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    const bool small_kernel = small && p->N > TIDE_SMALL_FEW_RANKS;
+    RsShape r;
+    r.small_kernel = small_kernel;
+    r.tiles = static_cast<const Tile *>(small_kernel ? ds->d_rs_tiles_small : ds->d_rs_tiles);
+    r.ntiles = static_cast<int64_t>(small_kernel ? p->rs_tiles_small.size() : p->rs_tiles.size());
+    r.lds = small ? ds->small_lds : ds->rs_cap_lds;
+    return r;
+}
+
 // Whether work enqueued on `stream` is being captured into a graph.
 tide_status capture_status(void *stream, bool *capturing) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -449,13 +478,10 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
                              static_cast<hipStream_t>(stream), capturing, &pt);
     if (st != TIDE_OK) return st;
 
-    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
-    const int64_t ntiles =
-        static_cast<int64_t>(small ? plan->rs_tiles_small.size() : plan->rs_tiles.size());
+    const tide::RsShape shape = tide::rs_shape(plan, ds, flags);
     const tide::RsLaunch L{static_cast<const tide::ParamDesc *>(ds->d_params),
-                           static_cast<const tide::Tile *>(small ? ds->d_rs_tiles_small
-                                                                 : ds->d_rs_tiles),
-                           ntiles,
+                           shape.tiles,
+                           shape.ntiles,
                            static_cast<const char *const *>(pt->dev),
                            plan->N,
                            rank,
@@ -463,14 +489,14 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
                            out,
                            pt->aligned16 ? 1 : 0,
                            (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
-                           tide::grid_size(ds, ntiles, flags, max_workgroups),
-                           small ? ds->small_lds : ds->rs_cap_lds,
+                           tide::grid_size(ds, shape.ntiles, flags, max_workgroups),
+                           shape.lds,
                            static_cast<hipStream_t>(stream)};
     const tide::GradType type = (flags & TIDE_F_GRAD_F32)   ? tide::kF32
                                 : (flags & TIDE_F_GRAD_F16) ? tide::kF16
                                                             : tide::kBf16;
     const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
-    hipError_t e = tide::launch_rs(L, type, otype, small);
+    hipError_t e = tide::launch_rs(L, type, otype, shape.small_kernel);
     if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
     st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;
@@ -689,13 +715,10 @@ extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
                              static_cast<hipStream_t>(stream), capturing, &pt);
     if (st != TIDE_OK) return st;
 
-    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
-    const int64_t ntiles =
-        static_cast<int64_t>(small ? plan->rs_tiles_small.size() : plan->rs_tiles.size());
+    const tide::RsShape shape = tide::rs_shape(plan, ds, flags);
     const tide::RsLaunch L{static_cast<const tide::ParamDesc *>(ds->d_params),
-                           static_cast<const tide::Tile *>(small ? ds->d_rs_tiles_small
-                                                                 : ds->d_rs_tiles),
-                           ntiles,
+                           shape.tiles,
+                           shape.ntiles,
                            static_cast<const char *const *>(pt->dev),
                            N,
                            rank,
@@ -703,14 +726,14 @@ extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
                            out,
                            pt->aligned16 ? 1 : 0,
                            (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
-                           tide::grid_size(ds, ntiles, flags, max_workgroups),
-                           small ? ds->small_lds : ds->rs_cap_lds,
+                           tide::grid_size(ds, shape.ntiles, flags, max_workgroups),
+                           shape.lds,
                            static_cast<hipStream_t>(stream)};
     const tide::GradType type = (flags & TIDE_F_GRAD_F32)   ? tide::kF32
                                 : (flags & TIDE_F_GRAD_F16) ? tide::kF16
                                                             : tide::kBf16;
     const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
-    hipError_t e = tide::launch_rs(L, type, otype, small);
+    hipError_t e = tide::launch_rs(L, type, otype, shape.small_kernel);
     if (e != hipSuccess) return tide::hip_fail("tide_rs_slots: kernel launch", e);
     st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;
