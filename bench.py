@@ -544,6 +544,24 @@ def corun_rs(w, gemm):
     return res
 
 
+def corun_rs_step(step, gemm):
+    """tide_rs beside the GEMM on the step's workload (its gradients are
+    already resident), default and small-footprint launch."""
+    plan, N = step.plan, step.w.world
+    res = {"gemm": gemm.name, "gemm_alone_ms": gemm.alone_ms, "workload": step.w.name,
+           "world": N, "method": CORUN_METHOD}
+    for small in (False, True):
+        key = "small_footprint" if small else "default"
+        r = corun_chain(gemm, lambda k, st: tide.rs(plan, k % N, step.table, step.blocks[k % N],
+                                                     small=small, stream=st), step.b_rs)
+        res[key] = {"tide_rs_alone_us": r["alone_us"], "tide_rs_alone_GBps": r["alone_GBps"],
+                    "tide_rs_corun_GBps": r["corun_GBps"],
+                    "gemm_slowdown_pct": r["gemm_slowdown_pct"], "runs": r["runs"]}
+        log(f"co-run tide_rs ({step.w.name}) {key}: slowdown {fmt(r['gemm_slowdown_pct'])}%, "
+            f"{r['corun_GBps']:.0f} GB/s during, {r['alone_GBps']:.0f} GB/s alone")
+    return res
+
+
 def corun_ag(step, gemm):
     """tide_ag beside the GEMM: kernel (default, small footprint) and SDMA copy engine."""
     res = {"gemm": gemm.name, "gemm_alone_ms": gemm.alone_ms, "workload": step.w.name,
@@ -705,12 +723,13 @@ def main():
     if copy_gbps:
         log(f"copy ceiling {copy_gbps:.1f} GB/s (torch), {fmt(copy_lib_gbps)} GB/s (library)")
     cpu = None if args.no_cpu else cpu_baseline(step)
-    corun_res = corun_ag_res = None
+    corun_res = corun_ag_res = corun_rs_step_res = None
     gemm = None
     if args.corun != "none":
         cw = workloads.WORKLOADS[args.corun]
         gemm = Gemm(cw.corun_gemm or (8192, 8192, 8192))
         corun_ag_res = corun_ag(step, gemm)
+        corun_rs_step_res = corun_rs_step(step, gemm)
     P, S = step.plan.P, step.plan.S
     del step
     gc.collect()
@@ -758,6 +777,7 @@ def main():
         "layout_conversion": layout,
         "corun": corun_res,
         "corun_ag": corun_ag_res,
+        "corun_rs_step_workload": corun_rs_step_res,
         "gemm_slowdown_pct": None if not corun_res else {
             k: corun_res[k]["gemm_slowdown_pct"] for k in ("default", "small_footprint")
             if k in corun_res},
