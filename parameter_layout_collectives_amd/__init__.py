@@ -112,6 +112,12 @@ class PointerTable:
         self.array = (ctypes.c_void_p * max(len(self.tensors), 1))(
             *[t.data_ptr() if t is not None else None for t in self.tensors])
 
+    def check_len(self, n, what):
+        """The library reads exactly n entries: refuse a table of another size."""
+        if len(self.tensors) != n:
+            raise ValueError(f"{what}: pointer table has {len(self.tensors)} entries, "
+                             f"the plan needs {n}")
+
 
 def grad_table(plan, grads):
     """PointerTable for tide_rs: grads[r][i] = rank r's gradient of param i,
@@ -159,6 +165,7 @@ def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=F
     rounded once to bf16.  avg: write the mean (sum / N) instead of the sum."""
     if not isinstance(grads, PointerTable):
         grads = grad_table(plan, grads)
+    grads.check_len(plan.world * plan.P, "rs")
     if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_cuda \
             or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 or bfloat16 device tensor")
@@ -213,6 +220,8 @@ def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, table
     tables: optional result of ag_tables() to skip re-marshalling.
     copy_engine: place the shards with SDMA copies instead of a kernel."""
     src_t, dst_t, e = tables if tables is not None else ag_tables(plan, rank_src, params)
+    src_t.check_len(plan.world, "ag (rank blocks)")
+    dst_t.check_len(plan.P, "ag (parameters)")
     flags = (SMALL_FOOTPRINT if small else 0) | (COPY_ENGINE if copy_engine else 0)
     _check(lib().tide_ag(plan.handle, src_t.array, dst_t.array, e, flags, int(max_workgroups),
                          _stream_handle(stream)))
@@ -243,6 +252,7 @@ def pack(plan, tensors, slot, small=False, max_workgroups=0, stream=None):
                 raise ValueError(f"tensors[{i}] has {t.numel()} elements, "
                                  f"expected {_numel(plan.shapes[i])}")
         tensors = PointerTable(tensors, slot.dtype)
+    tensors.check_len(plan.P, "pack")
     if slot.dtype not in _ELEM:
         raise TypeError(f"unsupported element type {slot.dtype}")
     _slot_size_ok(plan, slot, "slot")
@@ -277,6 +287,7 @@ def rs_slots(plan, rank, slots, out, small=False, max_workgroups=0, stream=None,
     were packed from.  out, small, avg: as for rs()."""
     if not isinstance(slots, PointerTable):
         slots = slot_table(plan, slots)
+    slots.check_len(plan.world, "rs_slots")
     if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_cuda \
             or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 or bfloat16 device tensor")

@@ -278,3 +278,20 @@ def test_custom_ops_registered():
     assert "Tensor(a2!)[] params" in schemas["ag"]
     assert "Tensor(a2!) slot" in schemas["pack"]
     assert "Tensor(a3!) out" in schemas["rs_slots"]
+
+
+def test_binding_refuses_pointer_tables_of_another_plan():
+    """A table built for another plan would make the library read past the
+    end of the host array: the binding refuses it before any call."""
+    import torch
+    plan = tide.Plan([(4, 4), (8,)], 2)                 # N*P = 4
+    other = tide.PointerTable([torch.zeros(1)] * 6)      # 6 entries (CPU tensors, never read)
+    out = torch.zeros(plan.S)
+    with pytest.raises(ValueError, match="pointer table"):
+        tide.rs(plan, 0, other, out)
+    with pytest.raises(ValueError, match="pointer table"):
+        tide.ag(plan, None, None, tables=(other, other, 2))
+    with pytest.raises(ValueError, match="pointer table"):
+        tide.pack(plan, other, torch.zeros(2 * plan.S))
+    with pytest.raises(ValueError, match="pointer table"):
+        tide.rs_slots(plan, 0, other, out)
