@@ -1,7 +1,8 @@
 """The collectives captured into a HIP graph (torch.cuda.graph) and replayed.
 
-One step (tide_rs for every rank in both launch modes, tide_ag, tide_pack
-and tide_rs_slots) is captured once and replayed three times.  Between
+One step (tide_rs for every rank in both launch modes, tide_ag as a kernel
+and on the copy engines, tide_pack and tide_rs_slots) is captured once and
+replayed three times.  Between
 replays the program does eager work of its own (new gradient and gathered
 values written in place, outputs refilled) and synchronises; every replay
 is checked against the oracle.  A pointer set the plan has not cached is
@@ -40,6 +41,8 @@ def test_step_captured_and_replayed(orc):
     gathered = torch.empty(N * S, dtype=torch.bfloat16, device=DEV)
     params = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
     agt = tide.ag_tables(plan, gathered, params)
+    params_ce = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
+    agt_ce = tide.ag_tables(plan, gathered, params_ce)
     slots = torch.empty(N, N * S, dtype=torch.bfloat16, device=DEV)
     stable = tide.slot_table(plan, slots)
     ptabs = [tide.PointerTable(grads[r], torch.bfloat16) for r in range(N)]
@@ -50,6 +53,7 @@ def test_step_captured_and_replayed(orc):
             tide.rs(plan, R, table, out[R])
             tide.rs(plan, R, table, out_small[R], small=True)
         tide.ag(plan, None, None, tables=agt)
+        tide.ag(plan, None, None, tables=agt_ce, copy_engine=True)
         for r in range(N):
             tide.pack(plan, ptabs[r], slots[r])
         tide.rs_slots(plan, 2, stable, out_slots)
@@ -76,7 +80,7 @@ def test_step_captured_and_replayed(orc):
         out.view(torch.int32).fill_(F32_SENTINEL)
         out_small.view(torch.int32).fill_(F32_SENTINEL)
         out_slots.view(torch.int32).fill_(F32_SENTINEL)
-        for p in params:
+        for p in params + params_ce:
             p.view(torch.int16).fill_(BF16_SENTINEL)
         torch.cuda.synchronize()
         note(f"graph: replay {rep}")
@@ -92,6 +96,8 @@ def test_step_captured_and_replayed(orc):
         want_p = orc.ag(shapes, N, [host[r * S:(r + 1) * S] for r in range(N)])
         for i, p in enumerate(params):
             assert np.array_equal(bits16(p).reshape(-1), want_p[i]), (rep, i)
+        for i, p in enumerate(params_ce):
+            assert np.array_equal(bits16(p).reshape(-1), want_p[i]), (rep, i, "copy engine")
 
     # a new pointer set cannot be uploaded inside a capture
     other = [[t.to(DEV) for t in rank]
