@@ -20,9 +20,18 @@ Reported (one JSON line on stdout, progress on stderr):
   corun       slowdown of a bf16 8192^3 GEMM on another stream while
               tide_rs runs (default and small-footprint launch) on the
               64-rank 70B layer;
+  corun_rs_step_workload  the same on the step's 8-rank workload;
   corun_ag    the same for tide_ag on the step's workload: kernel (default,
               small footprint) and SDMA copy engine;
-  cpu_baseline the CPU oracle on the same step's inputs (host cores).
+  small_footprint_alone   small-footprint launches with nothing beside them;
+  tide_rs_variants        the bf16 shard and the mean;
+  two_stage_rs            tide_pack + tide_rs_slots (one GPU's share);
+  layout_conversion       a decoder-layer step's forward+backward beside
+              FSDP2's layout copies (which TIDE removes) and this rank's
+              tide_rs + tide_ag;
+  copy ceilings           torch's device copy and the library's own copy;
+  cpu_baseline the CPU oracle on the same step's inputs (host cores), and
+              the tiny workload's step on one thread.
 
 Algorithmic bytes (what the method must move; the fp32 pack buffer and the
 copy-out pass it avoids are not counted):
