@@ -142,3 +142,40 @@ def test_llama70b_layer_64_ranks(orc):
             assert same_f32(got, wants[R]), (R, small, first_mismatch(got, wants[R]))
     del grads, table, a, b, outs
     _free()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_llama8b_layer_typed_gradients_and_mean(orc, dtype):
+    """The gradient-type and mean variants at full size: the 8B-shaped layer
+    with fp16 or fp32 gradients (the bf16 draws widened), sum and mean,
+    both launch modes, whole blocks of ranks 0 and 7 against the oracle."""
+    w = workloads.WORKLOADS["llama3_8b_layer"]
+    N = w.world
+    tdt = {"f16": torch.float16, "f32": torch.float32}[dtype]
+    note(f"{w.name}: {dtype} gradients on the device")
+    grads = [[t.to(tdt) for t in rank] for rank in workloads.all_grads(w, device=DEV)]
+    plan = tide.Plan(w.shapes, N)
+    table = tide.grad_table(plan, grads)
+    out = torch.empty(plan.S, dtype=torch.float32, device=DEV)
+    for R in (0, N - 1):
+        slices = []
+        for rank in grads:
+            row = []
+            for i, g in enumerate(rank):
+                src, L = plan.real(R, i)
+                h = g.reshape(-1)[src:src + L].cpu()
+                row.append(h.numpy() if dtype == "f32" else
+                           h.view(torch.int16).numpy().view(np.uint16))
+            slices.append(row)
+        for avg in (False, True):
+            want = orc.rs_slices(w.shapes, N, R, slices, dtype=dtype, avg=avg)
+            for small in (False, True):
+                out.view(torch.int32).fill_(F32_SENTINEL)
+                note(f"{w.name}: tide_rs {dtype} R={R} avg={avg} small={small}")
+                tide.rs(plan, R, table, out, small=small, avg=avg)
+                torch.cuda.synchronize()
+                got = out.cpu().numpy()
+                assert same_f32(got, want), (dtype, R, avg, small, first_mismatch(got, want))
+    del grads, table, out
+    _free()
