@@ -286,10 +286,10 @@ def _rmsnorm(x, w, eps=1e-5):
 def decoder_layer_fwd_bwd(p, x, n_heads, n_kv):
     """Forward and backward of one Llama-shaped decoder layer on one
     micro-batch x [T, D] with bf16 weights p = (q, k, v, o, gate, up, down,
-    norm1, norm2).  Every product is a 2-D GEMM: the attention core is an
-    elementwise stand-in (sigmoid(q * k) * v per head, k and v shared by
-    groups of heads) with the real parameters and gradient shapes, because
-    batched bf16 products can fault on these GPUs."""
+    norm1, norm2).  Every product is a plain 2-D GEMM: the attention core is
+    an elementwise stand-in (sigmoid(q * k) * v per head, k and v shared by
+    groups of heads) with the real parameters and gradient shapes, so no
+    batched bf16 product (or its transposed-operand backward) runs."""
     q_w, k_w, v_w, o_w, g_w, u_w, d_w, n1, n2 = p
     T = x.shape[0]
     hd = q_w.shape[0] // n_heads
