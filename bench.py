@@ -39,6 +39,7 @@ copy-out pass it avoids are not counted):
   tide_ag:  2 * Psi (bf16 reads)  +  2 * Psi (bf16 writes)
 """
 import argparse
+import dataclasses
 import gc
 import hashlib
 import json
@@ -53,6 +54,7 @@ sys.path.insert(0, ROOT)
 import torch  # noqa: E402
 
 import parameter_layout_collectives_amd as tide  # noqa: E402
+import parameter_layout_collectives_amd._lib as tide_lib  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
@@ -398,15 +400,20 @@ def kernel_stats(name, nbytes, times):
     }
 
 
-def counter_traffic(kernel):
+def counter_traffic(kernel, workload, small, other_lib):
     """HBM bytes per launch from the committed counter profile, if it was
-    taken on the current kernel source (else None)."""
+    taken on the current kernel source, on this workload and launch mode,
+    with the in-tree library (else None)."""
+    if other_lib:
+        return None
     try:
         with open(PMC_SUMMARY) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
     if doc.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if doc.get("workload") != workload or doc.get("launch") != ("small" if small else "default"):
         return None
     k = doc.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -679,6 +686,11 @@ def main():
     ap.add_argument("--no-lib-copy", action="store_true",
                     help="measure the copy ceiling with torch's copy only (profiled runs: the "
                          "library's copy is an all-gather launch)")
+    ap.add_argument("--world", type=int, default=0,
+                    help="number of emulated ranks, overriding the workload's (same shapes)")
+    ap.add_argument("--lib", default="",
+                    help="load this build of libtide.so instead of the in-tree one (e.g. one "
+                         "built with other tuning macros)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the tide_rs flag variants (bf16 shard, mean) and the "
                          "two-stage reduce-scatter")
@@ -692,9 +704,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no HIP device", file=sys.stderr, flush=True)
         sys.exit(1)
+    if args.lib:
+        tide_lib.LIB_PATH = os.path.abspath(args.lib)
     tide.lib()   # fails loudly if the HIP library is missing
 
     w = workloads.WORKLOADS[args.workload]
+    if args.world and args.world != w.world:
+        w = dataclasses.replace(w, name=f"{w.name}_n{args.world}", world=args.world)
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name}, {props.multi_processor_count} CUs")
 
@@ -710,7 +726,7 @@ def main():
         f"ag {ag_k['GBps']:.1f} GB/s")
 
     dom = rs_k if sum(t_rs) >= sum(t_ag) else ag_k
-    traffic = counter_traffic(dom["kernel"])
+    traffic = counter_traffic(dom["kernel"], w.name, args.small, bool(args.lib))
     roofline = {
         "bound": "hbm",
         "kernel": dom["kernel"],
@@ -795,6 +811,8 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    if args.lib:
+        line["library"] = args.lib
     print(json.dumps(line), flush=True)
 
 

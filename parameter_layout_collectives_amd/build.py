@@ -1,6 +1,10 @@
 """Build libtide.so (the TIDE C-ABI library) for gfx950 with hipcc.
 
-    python -m parameter_layout_collectives_amd.build
+    python -m parameter_layout_collectives_amd.build [--out PATH] [-D NAME=VALUE ...]
+
+-D overrides a tuning macro of the kernels or the launch policy (for
+experiments; the in-tree library is always built with the defaults), --out
+writes the library elsewhere than the package directory.
 
 Flags:
   * --offload-arch=gfx950: CDNA4 only;
@@ -47,6 +51,20 @@ def build(verbose=False, out=LIB, extra=()):
     return out
 
 
+def main(argv=None):
+    import argparse
+    ap = argparse.ArgumentParser(description="build libtide.so for gfx950")
+    ap.add_argument("--out", default=LIB, help="library path (default: in the package)")
+    ap.add_argument("-D", dest="defines", action="append", default=[], metavar="NAME=VALUE",
+                    help="override a tuning macro, e.g. -D TIDE_RS_WG_CAP=4")
+    args = ap.parse_args(argv)
+    for d in args.defines:
+        name = d.split("=", 1)[0]
+        if not name.startswith("TIDE_") or not name[5:].replace("_", "").isalnum():
+            ap.error(f"-D {d}: only TIDE_* tuning macros can be overridden")
+    build(verbose=True, out=os.path.abspath(args.out), extra=[f"-D{d}" for d in args.defines])
+    return 0
+
+
 if __name__ == "__main__":
-    build(verbose=True)
-    sys.exit(0)
+    sys.exit(main())
