@@ -280,6 +280,39 @@ def test_custom_ops_registered():
     assert "Tensor(a3!) out" in schemas["rs_slots"]
 
 
+@pytest.mark.filterwarnings("ignore:.*LeafSpec.*:FutureWarning")   # torch.export's own pytree use
+def test_custom_ops_trace_with_their_mutations():
+    """torch.export traces a step that calls tide::rs then tide::ag and reads
+    the reduce-scatter's output (fake tensors only: no kernel runs).  After
+    functionalization the graph records `out` and every parameter as mutated
+    inputs, and the read after the reduce-scatter takes its result."""
+    import torch
+    import parameter_layout_collectives_amd.torch_ops as tops
+    shapes = [(5, 7), (16,), (33, 4)]
+    plan = tide.Plan(shapes, 4)
+    pid = tops.register_plan(plan)
+    try:
+        class Step(torch.nn.Module):
+            def forward(self, flat, out, gathered, params):
+                torch.ops.tide.rs(pid, 1, flat, out, False, False)
+                torch.ops.tide.ag(pid, gathered, params, False, False)
+                return out * 2.0
+
+        flat = [torch.zeros(s, dtype=torch.bfloat16) for _ in range(4) for s in shapes]
+        out = torch.zeros(plan.S)
+        gathered = torch.zeros(4 * plan.S, dtype=torch.bfloat16)
+        params = [torch.zeros(s, dtype=torch.bfloat16) for s in shapes]
+        ep = torch.export.export(Step(), (flat, out, gathered, params)).run_decompositions()
+        mutated = ep.graph_signature.user_inputs_to_mutate
+        assert sorted(mutated.values()) == ["out", "params_0", "params_1", "params_2"]
+        code = ep.graph_module.code
+        assert "tide.rs.default" in code and "tide.ag.default" in code
+        rs_result = [k for k, v in mutated.items() if v == "out"][0]
+        assert f"aten.mul.Tensor({rs_result}, 2.0)" in code
+    finally:
+        tops.unregister_plan(pid)
+
+
 def test_binding_refuses_pointer_tables_of_another_plan():
     """A table built for another plan would make the library read past the
     end of the host array: the binding refuses it before any call."""

@@ -2,7 +2,7 @@
 custom operators and the FSDP-unit helper.
 
 * torch.ops.tide.{rs, ag, pack, rs_slots} give the same bits as the plain
-  binding;
+  binding, also inside a torch.compile'd step;
 * one optimizer step of a TideUnit (shard, reduce-scatter the mean of the
   ranks' gradients, SGD on the fp32 master shards, all-gather into bf16
   parameter storage) equals the same step composed from the oracle's
@@ -68,6 +68,42 @@ def test_custom_ops_match_binding(orc):
         for x, y in zip(p1, p2):
             assert torch.equal(x.view(torch.int16), y.view(torch.int16))
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    finally:
+        tops.unregister_plan(pid)
+
+
+def test_custom_ops_under_torch_compile():
+    """A compiled step (dynamo + AOT functionalization, eager kernels) that
+    reduce-scatters, all-gathers and reads the shard gives the eager bits."""
+    shapes = LAYER
+    N = 4
+    plan = tide.Plan(shapes, N)
+    pid = tops.register_plan(plan)
+    try:
+        g = [[t.to(DEV) for t in rank]
+             for rank in workloads.random_grads_for_shapes(shapes, N, seed_base=9)]
+        flat = [t for rank in g for t in rank]
+        gathered = workloads.random_bf16(N * plan.S, seed=10, device=DEV)
+
+        def step(flat, out, gathered, params):
+            torch.ops.tide.rs(pid, 2, flat, out, False, True)
+            torch.ops.tide.ag(pid, gathered, params, False, False)
+            return out * 2.0
+
+        compiled = torch.compile(step, backend="aot_eager", fullgraph=True)
+        res = {}
+        for name, fn in (("eager", step), ("compiled", compiled)):
+            out = torch.full((plan.S,), float("nan"), device=DEV)
+            params = [torch.zeros(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
+            note(f"tide::rs + tide::ag, {name}")
+            y = fn(flat, out, gathered, params)
+            torch.cuda.synchronize()
+            res[name] = (out, params, y)
+        (o1, p1, y1), (o2, p2, y2) = res["eager"], res["compiled"]
+        assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+        for a, b in zip(p1, p2):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     finally:
         tops.unregister_plan(pid)
 
