@@ -689,7 +689,7 @@ def main():
     ap.add_argument("--world", type=int, default=0,
                     help="number of emulated ranks, overriding the workload's (same shapes)")
     ap.add_argument("--lib", default="",
-                    help="load this build of libtide.so instead of the in-tree one (e.g. one "
+                    help="load the libtide.so at this path instead of the in-tree one (e.g. one "
                          "built with other tuning macros)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the tide_rs flag variants (bf16 shard, mean) and the "
