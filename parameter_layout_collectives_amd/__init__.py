@@ -75,6 +75,8 @@ class Plan:
         self._h = h
         self.S = int(lib().tide_plan_shard_numel(h))
         self.P = P
+        # what a pointer table is checked against (compared by identity)
+        self._sig = (self.world, tuple(self.shapes), self.S)
 
     def __del__(self, _finalizing=sys.is_finalizing):
         # At interpreter exit the HIP runtime may already be torn down (and
@@ -104,13 +106,19 @@ class Plan:
 
 class PointerTable:
     """A host array of device pointers kept alive with the tensors it names.
-    Build it once and pass it to rs/ag repeatedly to skip re-marshalling."""
+    Build it once and pass it to rs/ag repeatedly to skip re-marshalling.
+
+    The kernels read as many bytes behind each pointer as the plan says, so
+    a table is checked against the plan (element counts, dtype, device,
+    contiguity) the first time it is used with that plan for a given call;
+    later calls with the same plan skip the check."""
 
     def __init__(self, tensors, dtype=None):
         self.tensors = list(tensors)
         self.dtype = dtype
         self.array = (ctypes.c_void_p * max(len(self.tensors), 1))(
             *[t.data_ptr() if t is not None else None for t in self.tensors])
+        self._checked = {}   # role -> signature of the plan it was checked against
 
     def check_len(self, n, what):
         """The library reads exactly n entries: refuse a table of another size."""
@@ -118,34 +126,43 @@ class PointerTable:
             raise ValueError(f"{what}: pointer table has {len(self.tensors)} entries, "
                              f"the plan needs {n}")
 
+    def _ensure(self, plan, role, check):
+        """Runs check() unless this table already passed it for this plan."""
+        if self._checked.get(role) is not plan._sig:
+            check()
+            self._checked[role] = plan._sig
+
+
+def _check_grads(plan, flat, dtype):
+    """flat[r*P + i] is rank r's gradient of param i: all of `dtype`."""
+    if dtype not in _GRAD_FLAG:
+        raise TypeError(f"gradients must be bfloat16, float16 or float32, got {dtype}")
+    for k, t in enumerate(flat):
+        if t.dtype != dtype:
+            r, i = divmod(k, plan.P)
+            raise TypeError(f"grads[{r}][{i}] is {t.dtype}, the others are {dtype}")
+    for k, t in enumerate(flat):
+        r, i = divmod(k, plan.P)
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"grads[{r}][{i}] must be a contiguous device tensor")
+        if t.numel() != _numel(plan.shapes[i]):
+            raise ValueError(f"grads[{r}][{i}] has {t.numel()} elements, "
+                             f"expected {_numel(plan.shapes[i])}")
+
 
 def grad_table(plan, grads):
     """PointerTable for tide_rs: grads[r][i] = rank r's gradient of param i,
     all bf16, all fp16 or all fp32."""
     if len(grads) != plan.world:
         raise ValueError(f"expected {plan.world} ranks of gradients, got {len(grads)}")
-    dtype = None
     for r, rank in enumerate(grads):
         if len(rank) != plan.P:
             raise ValueError(f"rank {r}: expected {plan.P} gradients, got {len(rank)}")
-        for i, t in enumerate(rank):
-            if t.dtype not in _GRAD_FLAG:
-                raise TypeError(f"grads[{r}][{i}] must be bfloat16, float16 or float32, "
-                                f"got {t.dtype}")
-            if dtype is None:
-                dtype = t.dtype
-            elif t.dtype != dtype:
-                raise TypeError(f"grads[{r}][{i}] is {t.dtype}, the others are {dtype}")
-    flat = []
-    for r, rank in enumerate(grads):
-        for i, t in enumerate(rank):
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"grads[{r}][{i}] must be a contiguous device tensor")
-            if t.numel() != _numel(plan.shapes[i]):
-                raise ValueError(f"grads[{r}][{i}] has {t.numel()} elements, "
-                                 f"expected {_numel(plan.shapes[i])}")
-            flat.append(t)
-    return PointerTable(flat, dtype)
+    flat = [t for rank in grads for t in rank]
+    dtype = flat[0].dtype if flat else torch.bfloat16
+    table = PointerTable(flat, dtype)
+    table._ensure(plan, "rs", lambda: _check_grads(plan, flat, dtype))
+    return table
 
 
 def _numel(shape):
@@ -166,6 +183,7 @@ def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=F
     if not isinstance(grads, PointerTable):
         grads = grad_table(plan, grads)
     grads.check_len(plan.world * plan.P, "rs")
+    grads._ensure(plan, "rs", lambda: _check_grads(plan, grads.tensors, grads.dtype))
     if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_cuda \
             or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 or bfloat16 device tensor")
@@ -181,6 +199,24 @@ def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=F
 _ELEM = {torch.bfloat16: 2, torch.float16: 2, torch.int16: 2, torch.float32: 4, torch.int32: 4}
 
 
+def _check_ag(plan, blocks, params, e):
+    """N rank blocks of at least S elements and P parameters of their sizes,
+    all contiguous device tensors of one dtype of e bytes."""
+    dt = blocks[0].dtype if blocks else None
+    if dt not in _ELEM or _ELEM[dt] != e:
+        raise TypeError(f"unsupported element type {dt} for {e}-byte elements")
+    for r, b in enumerate(blocks):
+        if b.dtype != dt or not b.is_cuda or not b.is_contiguous() or b.numel() < plan.S:
+            raise ValueError(f"rank block {r} must be a contiguous {dt} device tensor "
+                             f"of at least S elements")
+    for i, t in enumerate(params):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"params[{i}] must be a contiguous {dt} device tensor")
+        if t.numel() != _numel(plan.shapes[i]):
+            raise ValueError(f"params[{i}] has {t.numel()} elements, "
+                             f"expected {_numel(plan.shapes[i])}")
+
+
 def ag_tables(plan, rank_src, params):
     """(PointerTable of rank blocks, PointerTable of params, element bytes)."""
     if isinstance(rank_src, torch.Tensor):
@@ -193,22 +229,18 @@ def ag_tables(plan, rank_src, params):
         blocks = [flat[r * plan.S:(r + 1) * plan.S] for r in range(plan.world)]
     else:
         blocks = list(rank_src)
+    params = list(params)
     if len(blocks) != plan.world or len(params) != plan.P:
         raise ValueError("need one block per rank and one tensor per parameter")
     dt = blocks[0].dtype
     if dt not in _ELEM:
         raise TypeError(f"unsupported element type {dt}")
-    for r, b in enumerate(blocks):
-        if b.dtype != dt or not b.is_cuda or not b.is_contiguous() or b.numel() < plan.S:
-            raise ValueError(f"rank block {r} must be a contiguous {dt} device tensor "
-                             f"of at least S elements")
-    for i, t in enumerate(params):
-        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"params[{i}] must be a contiguous {dt} device tensor")
-        if t.numel() != _numel(plan.shapes[i]):
-            raise ValueError(f"params[{i}] has {t.numel()} elements, "
-                             f"expected {_numel(plan.shapes[i])}")
-    return PointerTable(blocks), PointerTable(params), _ELEM[dt]
+    e = _ELEM[dt]
+    _check_ag(plan, blocks, params, e)
+    src_t, dst_t = PointerTable(blocks), PointerTable(params)
+    src_t._checked["ag"] = plan._sig
+    dst_t._checked["ag"] = plan._sig
+    return src_t, dst_t, e
 
 
 def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, tables=None,
@@ -222,6 +254,9 @@ def ag(plan, rank_src, params, small=False, max_workgroups=0, stream=None, table
     src_t, dst_t, e = tables if tables is not None else ag_tables(plan, rank_src, params)
     src_t.check_len(plan.world, "ag (rank blocks)")
     dst_t.check_len(plan.P, "ag (parameters)")
+    if src_t._checked.get("ag") is not plan._sig or dst_t._checked.get("ag") is not plan._sig:
+        _check_ag(plan, src_t.tensors, dst_t.tensors, e)
+        src_t._checked["ag"] = dst_t._checked["ag"] = plan._sig
     flags = (SMALL_FOOTPRINT if small else 0) | (COPY_ENGINE if copy_engine else 0)
     _check(lib().tide_ag(plan.handle, src_t.array, dst_t.array, e, flags, int(max_workgroups),
                          _stream_handle(stream)))
@@ -235,6 +270,15 @@ def _slot_size_ok(plan, slot, what):
                          f"{plan.world * plan.S}")
 
 
+def _check_pack(plan, tensors, dtype):
+    for i, t in enumerate(tensors):
+        if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"tensors[{i}] must be a contiguous {dtype} device tensor")
+        if t.numel() != _numel(plan.shapes[i]):
+            raise ValueError(f"tensors[{i}] has {t.numel()} elements, "
+                             f"expected {_numel(plan.shapes[i])}")
+
+
 def pack(plan, tensors, slot, small=False, max_workgroups=0, stream=None):
     """Stage 1 of the two-stage TIDE-RS: lay one rank's per-parameter tensors
     out rank-major in `slot` (N*S elements of the tensors' dtype; for
@@ -242,24 +286,31 @@ def pack(plan, tensors, slot, small=False, max_workgroups=0, stream=None):
 
     tensors: list of P device tensors of one 2- or 4-byte dtype, or a
     PointerTable of them."""
+    if slot.dtype not in _ELEM:
+        raise TypeError(f"unsupported element type {slot.dtype}")
     if not isinstance(tensors, PointerTable):
         if len(tensors) != plan.P:
             raise ValueError(f"expected {plan.P} tensors, got {len(tensors)}")
-        for i, t in enumerate(tensors):
-            if t.dtype != slot.dtype or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"tensors[{i}] must be a contiguous {slot.dtype} device tensor")
-            if t.numel() != _numel(plan.shapes[i]):
-                raise ValueError(f"tensors[{i}] has {t.numel()} elements, "
-                                 f"expected {_numel(plan.shapes[i])}")
         tensors = PointerTable(tensors, slot.dtype)
     tensors.check_len(plan.P, "pack")
-    if slot.dtype not in _ELEM:
-        raise TypeError(f"unsupported element type {slot.dtype}")
+    if tensors.dtype is not None and tensors.dtype != slot.dtype:
+        raise TypeError(f"pack: tensors are {tensors.dtype}, the slot is {slot.dtype}")
+    tensors._ensure(plan, ("pack", slot.dtype), lambda: _check_pack(plan, tensors.tensors,
+                                                                    slot.dtype))
     _slot_size_ok(plan, slot, "slot")
     flags = SMALL_FOOTPRINT if small else 0
     _check(lib().tide_pack(plan.handle, tensors.array, ctypes.c_void_p(slot.data_ptr()),
                            _ELEM[slot.dtype], flags, int(max_workgroups),
                            _stream_handle(stream)))
+
+
+def _check_slots(plan, slots, dtype):
+    if dtype not in _GRAD_FLAG:
+        raise TypeError(f"slots must be bfloat16, float16 or float32, got {dtype}")
+    for r, t in enumerate(slots):
+        if t.dtype != dtype:
+            raise TypeError(f"slots[{r}] is {t.dtype}, the others are {dtype}")
+        _slot_size_ok(plan, t, f"slots[{r}]")
 
 
 def slot_table(plan, slots):
@@ -272,13 +323,10 @@ def slot_table(plan, slots):
     if len(slots) != plan.world:
         raise ValueError(f"expected {plan.world} slots, got {len(slots)}")
     dtype = slots[0].dtype
-    if dtype not in _GRAD_FLAG:
-        raise TypeError(f"slots must be bfloat16, float16 or float32, got {dtype}")
-    for r, t in enumerate(slots):
-        if t.dtype != dtype:
-            raise TypeError(f"slots[{r}] is {t.dtype}, the others are {dtype}")
-        _slot_size_ok(plan, t, f"slots[{r}]")
-    return PointerTable(slots, dtype)
+    _check_slots(plan, slots, dtype)
+    table = PointerTable(slots, dtype)
+    table._checked["rs_slots"] = plan._sig
+    return table
 
 
 def rs_slots(plan, rank, slots, out, small=False, max_workgroups=0, stream=None, avg=False):
@@ -288,6 +336,7 @@ def rs_slots(plan, rank, slots, out, small=False, max_workgroups=0, stream=None,
     if not isinstance(slots, PointerTable):
         slots = slot_table(plan, slots)
     slots.check_len(plan.world, "rs_slots")
+    slots._ensure(plan, "rs_slots", lambda: _check_slots(plan, slots.tensors, slots.dtype))
     if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_cuda \
             or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 or bfloat16 device tensor")

@@ -268,6 +268,62 @@ def test_python_binding_rejects_bad_tensors():
         tide.grad_table(plan, cpu[:1])
 
 
+class _DeviceStub:
+    """Passes the binding's tensor checks (device, contiguous, size, dtype)
+    but points at address 0, which the library refuses before enqueuing
+    anything: a check that wrongly let it through still launches nothing."""
+
+    is_cuda = True
+
+    def __init__(self, n, dtype):
+        self.n, self.dtype = n, dtype
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        return self.n
+
+    def data_ptr(self):
+        return 0
+
+
+def test_pointer_tables_are_checked_against_each_plan():
+    """A table whose tensors fit one plan is refused by another plan with
+    the same numbers of ranks and parameters but larger shapes: the kernels
+    would read past the ends of its tensors.  With its own plan it passes
+    the table checks and stops at the next check (a host `out`)."""
+    import torch
+    bf = torch.bfloat16
+    small = tide.Plan([(4, 4), (8,)], 2)
+    large = tide.Plan([(400, 400), (8,)], 2)
+    host_out = torch.zeros(large.S)
+
+    grads = tide.PointerTable([_DeviceStub(16, bf), _DeviceStub(8, bf)] * 2, bf)
+    with pytest.raises(ValueError, match="elements"):
+        tide.rs(large, 0, grads, host_out)
+    with pytest.raises(ValueError, match="out must be"):
+        tide.rs(small, 0, grads, torch.zeros(small.S))
+    with pytest.raises(ValueError, match="elements"):      # checked again for the other plan
+        tide.rs(large, 0, grads, host_out)
+    wrong_dtype = tide.PointerTable([_DeviceStub(16, bf), _DeviceStub(8, bf)] * 2, torch.float32)
+    with pytest.raises(TypeError):
+        tide.rs(small, 0, wrong_dtype, torch.zeros(small.S))
+
+    blocks = tide.PointerTable([_DeviceStub(small.S, bf)] * 2)
+    params = tide.PointerTable([_DeviceStub(16, bf), _DeviceStub(8, bf)])
+    with pytest.raises(ValueError):
+        tide.ag(large, None, None, tables=(blocks, params, 2))
+    with pytest.raises(TypeError):                          # 2-byte tensors, 4-byte elements
+        tide.ag(small, None, None, tables=(blocks, params, 4))
+
+    with pytest.raises(ValueError, match="elements"):
+        tide.pack(large, params, torch.zeros(2 * large.S, dtype=bf))
+    slots = tide.PointerTable([_DeviceStub(2 * small.S, bf)] * 2, bf)
+    with pytest.raises(ValueError, match="elements"):
+        tide.rs_slots(large, 0, slots, host_out)
+
+
 def test_custom_ops_registered():
     """The PyTorch operators exist and declare the tensors they write."""
     import torch
