@@ -24,6 +24,8 @@ Reported (one JSON line on stdout, progress on stderr):
   corun_ag    the same for tide_ag on the step's workload: kernel (default,
               small footprint) and SDMA copy engine;
   small_footprint_alone   small-footprint launches with nothing beside them;
+  tiny_gpu_latency        the tiny workload's step on the GPU, in microseconds
+              (per call, back to back, and per HIP-graph replay);
   tide_rs_variants        the bf16 shard and the mean;
   two_stage_rs            tide_pack + tide_rs_slots (one GPU's share);
   layout_conversion       a decoder-layer step's forward+backward beside
@@ -186,6 +188,76 @@ class Step:
         t_rs = [s.elapsed_time(e) * 1e-3 for s, e in ev_rs]
         t_ag = [s.elapsed_time(e) * 1e-3 for s, e in ev_ag]
         return wall, t_rs, t_ag
+
+
+def tiny_latency(reps=200, warmup=20, replays=200):
+    """The tiny workload's step on the GPU (tide_rs for its rank, then tide_ag
+    of the fp32 blocks): a few hundred bytes, so it is latency-bound and
+    reported in microseconds, with no roofline.  Three figures: the median
+    event-timed duration of each call, the wall time per step launched back
+    to back from Python (bound by the host cost of the calls), and the wall
+    time per replay of a HIP graph holding the step, replayed back to back
+    (the graph launch path instead of two kernel launches)."""
+    w = workloads.WORKLOADS["tiny"]
+    N, R = w.world, w.rank
+    grads = workloads.all_grads(w, device="cuda")
+    plan = tide.Plan(w.shapes, N)
+    table = tide.grad_table(plan, grads)
+    blocks = torch.zeros(N, plan.S, dtype=torch.float32, device="cuda")
+    params = [torch.empty(s, dtype=torch.float32, device="cuda") for s in w.shapes]
+    agt = tide.ag_tables(plan, blocks, params)
+
+    def rs():
+        tide.rs(plan, R, table, blocks[R])
+
+    def ag():
+        tide.ag(plan, None, None, tables=agt)
+
+    for _ in range(warmup):
+        rs()
+        ag()
+    torch.cuda.synchronize()
+    ev_rs, ev_ag = timed_events(reps), timed_events(reps)
+    for k in range(reps):
+        ev_rs[k][0].record()
+        rs()
+        ev_rs[k][1].record()
+        ev_ag[k][0].record()
+        ag()
+        ev_ag[k][1].record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rs()
+        ag()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    res = {
+        "workload": w.name,
+        "rank": R,
+        "tide_rs_event_us_median": statistics.median(s.elapsed_time(e) for s, e in ev_rs) * 1e3,
+        "tide_ag_event_us_median": statistics.median(s.elapsed_time(e) for s, e in ev_ag) * 1e3,
+        "step_wall_us_back_to_back": wall * 1e6,
+    }
+    # the same step captured once (its pointer tables are already uploaded)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rs()
+        ag()
+    torch.cuda.synchronize()
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    res["step_us_graph_replay"] = (time.perf_counter() - t0) / replays * 1e6
+    del g
+    log(f"tiny step: rs {res['tide_rs_event_us_median']:.1f} us, ag "
+        f"{res['tide_ag_event_us_median']:.1f} us (events), {res['step_wall_us_back_to_back']:.1f} "
+        f"us back to back, {res['step_us_graph_replay']:.1f} us per graph replay")
+    return res
 
 
 def small_footprint_alone(step, reps=20, warmup=3):
@@ -741,6 +813,7 @@ def main():
 
     variants = None if args.no_variants else rs_variants(step)
     small_alone = None if args.no_variants else small_footprint_alone(step)
+    tiny = None if args.no_variants else tiny_latency()
     two_stage = None if args.no_variants else two_stage_leg(step)
     layout = None if args.no_variants else layout_conversion_leg(step)
     copy_gbps, copy_lib_gbps = (None, None) if args.no_copy else \
@@ -801,6 +874,7 @@ def main():
         "tide_ag": ag_k,
         "tide_rs_variants": variants,
         "small_footprint_alone": small_alone,
+        "tiny_gpu_latency": tiny,
         "two_stage_rs": two_stage,
         "layout_conversion": layout,
         "corun": corun_res,
