@@ -257,6 +257,34 @@ tide_status tide_rs_slots(const tide_plan *plan, int32_t rank, const void *const
                           void *out, uint32_t flags, int32_t max_workgroups, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Allocation-free TIDE-RS.                                                */
+/* ---------------------------------------------------------------------- */
+
+/* tide_rs for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, flags, validation and result as tide_rs, bit for bit; it
+ * calls no hipMalloc, hipFree or other allocating HIP routine and keeps no
+ * per-plan device state.  The tables tide_rs keeps in plan-owned device
+ * memory (parameter descriptors, tile list, pointer table) are instead
+ * written, on `stream`, into one fixed 8 MiB array per device that the
+ * library holds until the process ends; the first call on a device only
+ * looks up that array's address.  Each call enqueues small table-writing
+ * launches (the tables travel as kernel arguments, about 3.5 KiB per launch)
+ * and then the reduce-scatter kernel.
+ *   Limit: 32*P + 8*(P+1) + 8*(N*P + 32) bytes of tables, rounded up to 256,
+ *   plus 16 bytes per tile (ceil(span_i / 4096) tiles per parameter, or
+ *   ceil(span_i / 2048) with TIDE_F_SMALL_FOOTPRINT above 16 ranks) must fit
+ *   in 8 MiB; a larger plan returns TIDE_E_INVALID before anything is
+ *   enqueued.
+ *   Sharing: every call on one device uses that device's one array.  Calls
+ *   ordered on one stream are safe; calls that overlap on one device (other
+ *   streams, or other host threads without ordering between them) race on
+ *   the array and may read each other's tables.  Order them with events or
+ *   use one stream. */
+tide_status tide_rs_noalloc(const tide_plan *plan, int32_t rank, const void *const *grads,
+                            void *out, uint32_t flags, int32_t max_workgroups, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Diagnostics.                                                            */
 /* ---------------------------------------------------------------------- */
 

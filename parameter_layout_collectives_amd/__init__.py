@@ -172,14 +172,8 @@ def _numel(shape):
     return n
 
 
-def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=False):
-    """TIDE-RS: write rank `rank`'s block (plan.S elements) into `out`.
-
-    grads: list over ranks of lists over params of device tensors (bf16,
-    fp16 or fp32, one dtype for all), or a PointerTable from grad_table().
-    out: contiguous device tensor with plan.S elements (e.g. a row of an
-    [N, S] buffer): float32 for the fp32 shard, bfloat16 for the fp32 result
-    rounded once to bf16.  avg: write the mean (sum / N) instead of the sum."""
+def _rs_flags(plan, grads, out, small, avg):
+    """Checks rs()'s arguments and returns (pointer table, flags)."""
     if not isinstance(grads, PointerTable):
         grads = grad_table(plan, grads)
     grads.check_len(plan.world * plan.P, "rs")
@@ -192,8 +186,32 @@ def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=F
     flags = _GRAD_FLAG.get(grads.dtype, 0)
     flags |= (SMALL_FOOTPRINT if small else 0) | (AVG if avg else 0)
     flags |= OUT_BF16 if out.dtype == torch.bfloat16 else 0
+    return grads, flags
+
+
+def rs(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=False):
+    """TIDE-RS: write rank `rank`'s block (plan.S elements) into `out`.
+
+    grads: list over ranks of lists over params of device tensors (bf16,
+    fp16 or fp32, one dtype for all), or a PointerTable from grad_table().
+    out: contiguous device tensor with plan.S elements (e.g. a row of an
+    [N, S] buffer): float32 for the fp32 shard, bfloat16 for the fp32 result
+    rounded once to bf16.  avg: write the mean (sum / N) instead of the sum."""
+    grads, flags = _rs_flags(plan, grads, out, small, avg)
     _check(lib().tide_rs(plan.handle, int(rank), grads.array, ctypes.c_void_p(out.data_ptr()),
                          flags, int(max_workgroups), _stream_handle(stream)))
+
+
+def rs_noalloc(plan, rank, grads, out, small=False, max_workgroups=0, stream=None, avg=False):
+    """tide_rs_noalloc: rs() without any device allocation - its tables go
+    into the library's fixed per-device scratch array, rewritten on `stream`
+    by every call.  Same arguments and bit-identical result as rs().  Calls
+    that overlap on one device (other streams, unordered) race on that
+    array."""
+    grads, flags = _rs_flags(plan, grads, out, small, avg)
+    _check(lib().tide_rs_noalloc(plan.handle, int(rank), grads.array,
+                                 ctypes.c_void_p(out.data_ptr()), flags, int(max_workgroups),
+                                 _stream_handle(stream)))
 
 
 _ELEM = {torch.bfloat16: 2, torch.float16: 2, torch.int16: 2, torch.float32: 4, torch.int32: 4}
@@ -353,4 +371,4 @@ def rs_slots(plan, rank, slots, out, small=False, max_workgroups=0, stream=None,
 __all__ = ["Plan", "PointerTable", "TideError", "SMALL_FOOTPRINT", "COPY_ENGINE", "AVG",
            "GRAD_F16", "GRAD_F32", "OUT_BF16", "grad_table",
            "ag_tables", "slot_table",
-           "rs", "ag", "pack", "rs_slots", "lib"]
+           "rs", "rs_noalloc", "ag", "pack", "rs_slots", "lib"]

@@ -25,6 +25,7 @@ SIGNATURES = {
     "tide_ag": (_i32, [_p, _p, _p, _i32, _u32, _i32, _p]),
     "tide_pack": (_i32, [_p, _p, _p, _i32, _u32, _i32, _p]),
     "tide_rs_slots": (_i32, [_p, _i32, _p, _p, _u32, _i32, _p]),
+    "tide_rs_noalloc": (_i32, [_p, _i32, _p, _p, _u32, _i32, _p]),
     "tide_last_error": (ctypes.c_char_p, []),
     "tide_status_string": (ctypes.c_char_p, [_i32]),
 }

@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtide.so")
 
-SOURCES = ["plan.cpp", "runtime.hip", "kernels.hip"]
+SOURCES = ["plan.cpp", "runtime.hip", "kernels.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

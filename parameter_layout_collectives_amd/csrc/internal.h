@@ -36,14 +36,20 @@ struct PtrTable {
     uint64_t last_use = 0;
 };
 
-struct DeviceState {
-    int device = -1;
+// What the launch policy needs to know about one device, and the LDS
+// reservations it derives from that.
+struct DeviceLimits {
     int cus = 0;
     int lds_per_cu = 0;          // bytes of LDS per compute unit
     int lds_per_wg_max = 0;      // largest LDS allocation one workgroup may make
     int small_lds = 0;           // LDS a small-footprint workgroup reserves (0 = none)
     int rs_cap_lds = 0;          // LDS a default reduce-scatter workgroup reserves (0 = none)
     int ag_cap_lds = 0;          // LDS a default all-gather workgroup reserves (0 = none)
+};
+
+struct DeviceState {
+    int device = -1;
+    DeviceLimits lim;
     void *d_params = nullptr;    // ParamDesc[P]
     void *d_rs_tiles = nullptr;  // Tile[n_rs]
     void *d_ag_tiles = nullptr;  // Tile[n_ag]
@@ -101,5 +107,17 @@ tide_status check_rs_slots_args(const tide_plan *p, int32_t rank, const void *co
 
 // Frees the device tables of a plan (defined next to the kernels).
 void release_device_states(const tide_plan *p);
+
+// Launch policy (runtime.hip), shared by every entry point.
+tide_status query_limits(int device, DeviceLimits *out);   // device attributes (no allocation)
+// Kernel shape, tile size and LDS reservation of a reduce-scatter launch.
+struct RsPolicy {
+    bool small_kernel;   // the small-footprint kernel shape over kRsTileSmall tiles
+    int64_t tile;        // kRsTile or kRsTileSmall
+    int lds;
+};
+RsPolicy rs_policy(const DeviceLimits &lim, int32_t N, uint32_t flags);
+unsigned grid_size(const DeviceLimits &lim, int64_t ntiles, uint32_t flags, int32_t max_wg);
+tide_status hip_fail(const char *what, hipError_t e);
 
 }  // namespace tide

@@ -52,10 +52,6 @@ namespace {
 constexpr int kWgPerCu = TIDE_WG_PER_CU;      // default grid: enough waves to keep HBM busy
 constexpr int kSmallFootprintWg = TIDE_SMALL_WG;  // small-footprint grid
 
-tide_status hip_fail(const char *what, hipError_t e) {
-    return fail(TIDE_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
-}
-
 tide_status upload(const void *host, size_t bytes, void **dev, const char *what) {
     *dev = nullptr;
     if (bytes == 0) return TIDE_OK;
@@ -93,10 +89,10 @@ void free_state(DeviceState *ds) {
 }
 
 // LDS that lets exactly `cap` workgroups share a CU (0: no cap).
-int lds_for_cap(const DeviceState *ds, int cap) {
-    if (cap <= 0 || ds->lds_per_cu <= 0) return 0;
-    const int want = ds->lds_per_cu / cap - 1024;
-    return (want > 0 && want <= ds->lds_per_wg_max) ? want : 0;
+int lds_for_cap(const DeviceLimits &lim, int cap) {
+    if (cap <= 0 || lim.lds_per_cu <= 0) return 0;
+    const int want = lim.lds_per_cu / cap - 1024;
+    return (want > 0 && want <= lim.lds_per_wg_max) ? want : 0;
 }
 
 // The plan's tables on the current device (created on first use, which
@@ -115,34 +111,14 @@ tide_status device_state(const tide_plan *p, bool capturing, DeviceState **out) 
         return fail(TIDE_E_UNSUPPORTED,
                     "the first call of a plan on a device cannot be captured into a graph: "
                     "make one call outside the capture first");
+    DeviceLimits lim;
+    tide_status st = query_limits(dev, &lim);
+    if (st != TIDE_OK) return st;
     DeviceState *ds = new (std::nothrow) DeviceState;
     if (!ds) return fail(TIDE_E_NOMEM, "device state: out of host memory");
     ds->device = dev;
-    e = hipDeviceGetAttribute(&ds->cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipDeviceGetAttribute(&ds->lds_per_cu,
-                                  hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
-    if (e == hipSuccess)
-        e = hipDeviceGetAttribute(&ds->lds_per_wg_max, hipDeviceAttributeMaxSharedMemoryPerBlock,
-                                  dev);
-    if (e != hipSuccess) {
-        delete ds;
-        return hip_fail("hipDeviceGetAttribute", e);
-    }
-    // A small-footprint workgroup reserves just over half of a CU's LDS, so
-    // no two of them share a CU: the hardware dispatcher has to spread them
-    // one per CU, and a CU that holds one cannot take two workgroups of an
-    // LDS-heavy kernel running beside it.  The reservation is never touched.
-    ds->small_lds = 0;
-    if (TIDE_SMALL_LDS_RESERVE && ds->lds_per_cu > 0) {
-        const int want = ds->lds_per_cu / 2 + 1024;
-        if (want <= ds->lds_per_wg_max) ds->small_lds = want;
-    }
-    // Optional cap on default reduce-scatter workgroups per CU (same trick:
-    // an untouched LDS reservation of which exactly TIDE_RS_WG_CAP fit).
-    ds->rs_cap_lds = lds_for_cap(ds, TIDE_RS_WG_CAP);
-    ds->ag_cap_lds = lds_for_cap(ds, TIDE_AG_WG_CAP);
-    tide_status st = upload(p->desc.data(), p->desc.size() * sizeof(ParamDesc), &ds->d_params,
+    ds->lim = lim;
+    st = upload(p->desc.data(), p->desc.size() * sizeof(ParamDesc), &ds->d_params,
                             "parameter table");
     if (st == TIDE_OK)
         st = upload(p->rs_tiles.data(), p->rs_tiles.size() * sizeof(Tile), &ds->d_rs_tiles,
@@ -375,27 +351,6 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const P
     return TIDE_OK;
 }
 
-// Both launch modes give every tile its own short-lived workgroup, and the
-// hardware dispatcher balances them over all CUs.  Small-footprint launches
-// also reserve over half a CU's LDS per workgroup, so at most one of them
-// is resident on a CU at any moment: a concurrent GEMM keeps its place on
-// every CU and loses only a little issue bandwidth there.  max_wg > 0 caps
-// the grid (workgroups then loop over tiles).
-unsigned grid_size(const DeviceState *ds, int64_t ntiles, uint32_t flags, int32_t max_wg) {
-    int64_t g;
-    if (flags & TIDE_F_SMALL_FOOTPRINT)
-        g = !TIDE_SMALL_PERSISTENT ? ntiles
-            : ds->small_lds        ? static_cast<int64_t>(ds->cus) * TIDE_SMALL_WG_PER_CU
-                                   : kSmallFootprintWg;
-    else if (TIDE_DEFAULT_ONE_TILE_PER_WG)
-        g = ntiles;
-    else
-        g = static_cast<int64_t>(ds->cus) * kWgPerCu;
-    if (max_wg > 0) g = max_wg;
-    g = std::min<int64_t>({g, ntiles, 0x7fffffff});
-    return static_cast<unsigned>(std::max<int64_t>(g, 1));
-}
-
 // The reduce-scatter launch for `flags`: kernel shape, tile list, LDS.
 struct RsShape {
     bool small_kernel;   // the small-footprint kernel shape and its tile list
@@ -405,13 +360,13 @@ struct RsShape {
 };
 
 RsShape rs_shape(const tide_plan *p, const DeviceState *ds, uint32_t flags) {
-    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
-    const bool small_kernel = small && p->N > TIDE_SMALL_FEW_RANKS;
+    const RsPolicy pol = rs_policy(ds->lim, p->N, flags);
     RsShape r;
-    r.small_kernel = small_kernel;
-    r.tiles = static_cast<const Tile *>(small_kernel ? ds->d_rs_tiles_small : ds->d_rs_tiles);
-    r.ntiles = static_cast<int64_t>(small_kernel ? p->rs_tiles_small.size() : p->rs_tiles.size());
-    r.lds = small ? ds->small_lds : ds->rs_cap_lds;
+    r.small_kernel = pol.small_kernel;
+    r.tiles = static_cast<const Tile *>(pol.small_kernel ? ds->d_rs_tiles_small : ds->d_rs_tiles);
+    r.ntiles = static_cast<int64_t>(pol.small_kernel ? p->rs_tiles_small.size()
+                                                     : p->rs_tiles.size());
+    r.lds = pol.lds;
     return r;
 }
 
@@ -431,6 +386,67 @@ tide_status after_launch(PtrTable *pt, hipStream_t stream, bool capturing) {
 }
 
 }  // namespace
+
+tide_status hip_fail(const char *what, hipError_t e) {
+    return fail(TIDE_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+tide_status query_limits(int dev, DeviceLimits *out) {
+    DeviceLimits lim;
+    hipError_t e = hipDeviceGetAttribute(&lim.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&lim.lds_per_cu,
+                                  hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&lim.lds_per_wg_max, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                                  dev);
+    if (e != hipSuccess) return hip_fail("hipDeviceGetAttribute", e);
+    // A small-footprint workgroup reserves just over half of a CU's LDS, so
+    // no two of them share a CU: the hardware dispatcher has to spread them
+    // one per CU, and a CU that holds one cannot take two workgroups of an
+    // LDS-heavy kernel running beside it.  The reservation is never touched.
+    lim.small_lds = 0;
+    if (TIDE_SMALL_LDS_RESERVE && lim.lds_per_cu > 0) {
+        const int want = lim.lds_per_cu / 2 + 1024;
+        if (want <= lim.lds_per_wg_max) lim.small_lds = want;
+    }
+    // Optional cap on default reduce-scatter workgroups per CU (same trick:
+    // an untouched LDS reservation of which exactly TIDE_RS_WG_CAP fit).
+    lim.rs_cap_lds = lds_for_cap(lim, TIDE_RS_WG_CAP);
+    lim.ag_cap_lds = lds_for_cap(lim, TIDE_AG_WG_CAP);
+    *out = lim;
+    return TIDE_OK;
+}
+
+RsPolicy rs_policy(const DeviceLimits &lim, int32_t N, uint32_t flags) {
+    const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
+    RsPolicy r;
+    r.small_kernel = small && N > TIDE_SMALL_FEW_RANKS;
+    r.tile = r.small_kernel ? kRsTileSmall : kRsTile;
+    r.lds = small ? lim.small_lds : lim.rs_cap_lds;
+    return r;
+}
+
+// Both launch modes give every tile its own short-lived workgroup, and the
+// hardware dispatcher balances them over all CUs.  Small-footprint launches
+// also reserve over half a CU's LDS per workgroup, so at most one of them
+// is resident on a CU at any moment: a concurrent GEMM keeps its place on
+// every CU and loses only a little issue bandwidth there.  max_wg > 0 caps
+// the grid (workgroups then loop over tiles).
+unsigned grid_size(const DeviceLimits &lim, int64_t ntiles, uint32_t flags, int32_t max_wg) {
+    int64_t g;
+    if (flags & TIDE_F_SMALL_FOOTPRINT)
+        g = !TIDE_SMALL_PERSISTENT ? ntiles
+            : lim.small_lds        ? static_cast<int64_t>(lim.cus) * TIDE_SMALL_WG_PER_CU
+                                   : kSmallFootprintWg;
+    else if (TIDE_DEFAULT_ONE_TILE_PER_WG)
+        g = ntiles;
+    else
+        g = static_cast<int64_t>(lim.cus) * kWgPerCu;
+    if (max_wg > 0) g = max_wg;
+    g = std::min<int64_t>({g, ntiles, 0x7fffffff});
+    return static_cast<unsigned>(std::max<int64_t>(g, 1));
+}
 
 void release_device_states(const tide_plan *p) {
     std::lock_guard<std::mutex> lock(p->mu);
@@ -489,7 +505,7 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
                            out,
                            pt->aligned16 ? 1 : 0,
                            (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
-                           tide::grid_size(ds, shape.ntiles, flags, max_workgroups),
+                           tide::grid_size(ds->lim, shape.ntiles, flags, max_workgroups),
                            shape.lds,
                            static_cast<hipStream_t>(stream)};
     const tide::GradType type = (flags & TIDE_F_GRAD_F32)   ? tide::kF32
@@ -610,8 +626,8 @@ extern "C" tide_status tide_ag(const tide_plan *plan, const void *const *rank_sr
                            static_cast<const uintptr_t *>(pt->dev),
                            plan->N,
                            elem_bytes,
-                           tide::grid_size(ds, ntiles, flags, max_workgroups),
-                           small ? ds->small_lds : ds->ag_cap_lds,
+                           tide::grid_size(ds->lim, ntiles, flags, max_workgroups),
+                           small ? ds->lim.small_lds : ds->lim.ag_cap_lds,
                            static_cast<hipStream_t>(stream)};
     hipError_t e = tide::launch_ag(L, small);
     if (e != hipSuccess) return tide::hip_fail("tide_ag: kernel launch", e);
@@ -662,8 +678,8 @@ extern "C" tide_status tide_pack(const tide_plan *plan, const void *const *tenso
                              plan->P,
                              elem_bytes,
                              plan->S,
-                             tide::grid_size(ds, ntiles, flags, max_workgroups),
-                             small ? ds->small_lds : ds->ag_cap_lds,
+                             tide::grid_size(ds->lim, ntiles, flags, max_workgroups),
+                             small ? ds->lim.small_lds : ds->lim.ag_cap_lds,
                              static_cast<hipStream_t>(stream)};
     hipError_t e = tide::launch_pack(L, small);
     if (e != hipSuccess) return tide::hip_fail("tide_pack: kernel launch", e);
@@ -726,7 +742,7 @@ extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
                            out,
                            pt->aligned16 ? 1 : 0,
                            (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
-                           tide::grid_size(ds, shape.ntiles, flags, max_workgroups),
+                           tide::grid_size(ds->lim, shape.ntiles, flags, max_workgroups),
                            shape.lds,
                            static_cast<hipStream_t>(stream)};
     const tide::GradType type = (flags & TIDE_F_GRAD_F32)   ? tide::kF32

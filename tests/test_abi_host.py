@@ -384,3 +384,40 @@ def test_binding_refuses_pointer_tables_of_another_plan():
         tide.pack(plan, other, torch.zeros(2 * plan.S))
     with pytest.raises(ValueError, match="pointer table"):
         tide.rs_slots(plan, 0, other, out)
+
+
+def _rs_noalloc(plan, rank, grads, out, flags=0, max_wg=0):
+    return lib().tide_rs_noalloc(plan.handle if plan else None, rank, grads,
+                                 ctypes.c_void_p(out), flags, max_wg, None)
+
+
+def test_rs_noalloc_validates_like_tide_rs():
+    # the same checks as tide_rs, before anything reaches the HIP runtime
+    plan = tide.Plan([(4, 4), (8,)], 2)
+    good = _ptrs([A, A + 0x10000, A + 0x20000, A + 0x30000])
+    out = A + 0x100000
+    L = lib()
+    assert _rs_noalloc(None, 0, good, out) == E_INVALID
+    assert _rs_noalloc(plan, 2, good, out) == E_INVALID and b"rank" in L.tide_last_error()
+    assert _rs_noalloc(plan, 0, good, out, flags=0x2) == E_UNSUPPORTED
+    assert _rs_noalloc(plan, 0, None, out) == E_INVALID
+    assert _rs_noalloc(plan, 0, good, A + 0x20000 + 8) == E_INVALID
+    assert b"overlaps" in L.tide_last_error()
+    empty = tide.Plan([(0, 3)], 4)
+    assert _rs_noalloc(empty, 3, None, 0) == 0
+
+
+def test_rs_noalloc_rejects_tables_beyond_its_scratch():
+    L = lib()
+    # 2^32 elements in one parameter: 2^20 tiles of 4096 elements need 16 MiB
+    # of tile list, beyond the 8 MiB scratch array.
+    big = tide.Plan([(1 << 32,)], 1)
+    assert _rs_noalloc(big, 0, _ptrs([A]), A + (1 << 40)) == E_INVALID
+    msg = L.tide_last_error()
+    assert b"scratch" in msg and b"8388608" in msg
+    # 4096 ranks x 300 parameters: a 9.8 MB pointer table alone
+    N, P = 4096, 300
+    plan = tide.Plan([(N,)] * P, N)
+    ptrs = _ptrs([A + 16 * k for k in range(N * P)])
+    assert _rs_noalloc(plan, 0, ptrs, A + (1 << 36)) == E_INVALID
+    assert b"scratch" in L.tide_last_error()
