@@ -17,12 +17,17 @@ Reported (one JSON line on stdout, progress on stderr):
               launch time (HIP events on the launch stream) against the
               8 TB/s HBM peak, plus counter-measured traffic when a
               committed counter profile of the current kernel source exists;
-  corun       slowdown of a bf16 8192^3 GEMM on another stream while
-              tide_rs runs (default and small-footprint launch) on the
-              64-rank 70B layer;
+  corun       tide_rs (default and small-footprint launch) on the 64-rank
+              70B layer beside a bf16 8192^3 GEMM on another stream: the
+              GEMM's slowdown, the bytes the collective moves while the GEMMs
+              run (per-call events), and the exposed time of a fixed amount
+              of collective work run beside a fixed GEMM chain;
   corun_rs_step_workload  the same on the step's 8-rank workload;
   corun_ag    the same for tide_ag on the step's workload: kernel (default,
               small footprint) and SDMA copy engine;
+  corun_layer_step  tide_rs and tide_ag beside the decoder layer's own
+              forward+backward (8K tokens) instead of the GEMM;
+  corun_summary     one row per co-run leg and mode;
   small_footprint_alone   small-footprint launches with nothing beside them;
   tiny_gpu_latency        the tiny workload's step on the GPU, in microseconds
               (per call, back to back, and per HIP-graph replay);
@@ -312,13 +317,23 @@ def rs_variants(step, reps=20, warmup=3):
     return res
 
 
-def two_stage_leg(step, reps=16, warmup=2):
-    """One GPU's share of the two-stage TIDE-RS on the step's workload, R
-    rotating: stage 1 packs rank R's gradients into its rank-major slot
-    (2*Psi bytes read, 2*N*S written), stage 2 reduces block R of the N
-    slots (the peers' slots are packed beforehand, untimed).  Staging needs
-    N*S*2 bytes per rank, or none with Slot-Reuse (the vacated all-gather
-    buffer has exactly that size)."""
+def two_stage_leg(step, streams, reps=16, warmup=2, buckets=8):
+    """One GPU's share of the two-stage TIDE-RS on the step's workload.
+
+    Stage times, R rotating: stage 1 packs rank R's gradients into its
+    rank-major slot (2*Psi bytes read, 2*N*S written), stage 2 reduces block
+    R of the N slots (the peers' slots are packed beforehand, untimed).
+
+    Peak memory of rank R's reduce-scatter (torch.cuda.max_memory_allocated
+    above what is allocated before it): one-pass tide_rs; two-stage with a
+    staging slot of its own (allocated for the call); two-stage with
+    Slot-Reuse, where the slot is the vacated all-gather buffer.  The peers'
+    slots stand for other GPUs' memory and are allocated beforehand.
+
+    Pipelined bandwidth: `buckets` buckets (rank R = k mod N), two slot sets
+    used in turn, stage 1 of bucket k+1 on one stream while stage 2 of
+    bucket k runs on the other, against the same buckets one after the
+    other on one stream."""
     plan, N, S = step.plan, step.w.world, step.plan.S
     slots = torch.empty(N, N * S, dtype=torch.bfloat16, device="cuda")
     tables = [tide.PointerTable(step.grads[r], torch.bfloat16) for r in range(N)]
@@ -346,10 +361,102 @@ def two_stage_leg(step, reps=16, warmup=2):
     t = st1["mean_us"] + st2["mean_us"]
     log(f"two-stage: pack {st1['GBps']:.1f} GB/s, rs_slots {st2['GBps']:.1f} GB/s, "
         f"{t:.1f} us per rank vs one-pass")
-    del slots, stable, tables
+
+    # -- peak memory of rank R's reduce-scatter -----------------------------
+    R = 0
+
+    def extra_peak(fn):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        fn()
+        torch.cuda.synchronize()
+        return torch.cuda.max_memory_allocated() - base
+
+    def one_pass():
+        tide.rs(plan, R, step.table, out[R])
+
+    def with_slot(own):
+        tide.pack(plan, tables[R], own)
+        tbl = tide.slot_table(plan, [own if r == R else slots[r] for r in range(N)])
+        tide.rs_slots(plan, R, tbl, out[R])
+
+    def separate():
+        own = torch.empty(N * S, dtype=torch.bfloat16, device="cuda")
+        with_slot(own)
+        del own
+
+    mem = {
+        "peak_bytes_one_pass": extra_peak(one_pass),
+        "peak_bytes_separate": extra_peak(separate),
+        "peak_bytes_slot_reuse": extra_peak(lambda: with_slot(step.gathered)),
+        "staging_bytes_per_rank": 2 * N * S,
+        "method": "torch.cuda.max_memory_allocated() minus memory_allocated() before one "
+                  "rank's reduce-scatter; Slot-Reuse packs into the all-gather buffer",
+    }
+    log(f"two-stage peak memory: one-pass {mem['peak_bytes_one_pass']}, separate slot "
+        f"{mem['peak_bytes_separate']}, Slot-Reuse {mem['peak_bytes_slot_reuse']} bytes")
+
+    # -- pipelined: stage 1 of bucket k+1 beside stage 2 of bucket k --------
+    sets = [slots, slots.clone()]
+    stabs = [stable, tide.slot_table(plan, sets[1])]
+    sa, sb = streams
+    cur = torch.cuda.current_stream()
+
+    def run_buckets(pipelined):
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        if not pipelined:
+            for k in range(buckets):
+                Rk = k % N
+                tide.pack(plan, tables[Rk], sets[k % 2][Rk])
+                tide.rs_slots(plan, Rk, stabs[k % 2], out[Rk])
+        else:
+            sa.wait_stream(cur)
+            sb.wait_stream(cur)
+            packed = [torch.cuda.Event() for _ in range(buckets)]
+            reduced = [torch.cuda.Event() for _ in range(buckets)]
+            for k in range(buckets):
+                Rk = k % N
+                with torch.cuda.stream(sa):
+                    if k >= 2:
+                        sa.wait_event(reduced[k - 2])   # its slot set is read by bucket k-2
+                    tide.pack(plan, tables[Rk], sets[k % 2][Rk], stream=sa)
+                    packed[k].record(sa)
+                with torch.cuda.stream(sb):
+                    sb.wait_event(packed[k])
+                    tide.rs_slots(plan, Rk, stabs[k % 2], out[Rk], stream=sb)
+                    reduced[k].record(sb)
+            cur.wait_stream(sa)
+            cur.wait_stream(sb)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    run_buckets(False)
+    run_buckets(True)
+    seq = statistics.median(run_buckets(False) for _ in range(3))
+    pipe = statistics.median(run_buckets(True) for _ in range(3))
+    nbytes = buckets * (b1 + step.b_rs)
+    pipeline = {
+        "buckets": buckets,
+        "bytes_per_bucket": b1 + step.b_rs,
+        "sequential_ms": seq,
+        "pipelined_ms": pipe,
+        "sequential_GBps": nbytes / (seq * 1e-3) / 1e9,
+        "pipelined_GBps": nbytes / (pipe * 1e-3) / 1e9,
+    }
+    log(f"two-stage pipeline over {buckets} buckets: sequential {seq:.2f} ms "
+        f"({pipeline['sequential_GBps']:.0f} GB/s), pipelined {pipe:.2f} ms "
+        f"({pipeline['pipelined_GBps']:.0f} GB/s)")
+    del slots, stable, tables, sets, stabs
     return {"stage1_pack": st1, "stage2_rs_slots": st2, "total_us": t,
             "rs_effective_GBps": step.b_rs / (t * 1e-6) / 1e9,
-            "staging_bytes_per_rank": 2 * N * S, "staging_bytes_with_slot_reuse": 0}
+            "peak_memory": mem, "pipeline": pipeline,
+            "pipelined_GBps": pipeline["pipelined_GBps"],
+            "peak_bytes_separate": mem["peak_bytes_separate"],
+            "peak_bytes_slot_reuse": mem["peak_bytes_slot_reuse"]}
 
 
 def _rmsnorm(x, w, eps=1e-5):
@@ -357,21 +464,37 @@ def _rmsnorm(x, w, eps=1e-5):
     return (xf * torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)).to(x.dtype) * w
 
 
+def _attention(q, k, v):
+    """Causal attention of q [1, H, T, hd] over k, v [1, H, T, hd] through
+    PyTorch's fused SDPA kernels only (memory-efficient, else flash): the
+    unfused math path, which runs batched bf16 products, is never allowed."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    try:
+        with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION]):
+            return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    except RuntimeError:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+
+
 def decoder_layer_fwd_bwd(p, x, n_heads, n_kv):
     """Forward and backward of one Llama-shaped decoder layer on one
     micro-batch x [T, D] with bf16 weights p = (q, k, v, o, gate, up, down,
-    norm1, norm2).  Every product is a plain 2-D GEMM: the attention core is
-    an elementwise stand-in (sigmoid(q * k) * v per head, k and v shared by
-    groups of heads) with the real parameters and gradient shapes, so no
-    batched bf16 product (or its transposed-operand backward) runs."""
+    norm1, norm2): RMSNorm, q/k/v projections, causal attention (fused SDPA
+    with each k/v head shared by a group of query heads), output projection,
+    RMSNorm, SwiGLU MLP, residuals.  Rotary embeddings are left out (they
+    move no weights and add only elementwise work)."""
     q_w, k_w, v_w, o_w, g_w, u_w, d_w, n1, n2 = p
     T = x.shape[0]
     hd = q_w.shape[0] // n_heads
+    grp = n_heads // n_kv
     h = _rmsnorm(x, n1)
-    q = torch.nn.functional.linear(h, q_w).view(T, n_kv, n_heads // n_kv, hd)
-    k = torch.nn.functional.linear(h, k_w).view(T, n_kv, 1, hd)
-    v = torch.nn.functional.linear(h, v_w).view(T, n_kv, 1, hd)
-    a = (torch.sigmoid(q * k) * v).reshape(T, q_w.shape[0])
+    q = torch.nn.functional.linear(h, q_w).view(T, n_heads, hd).transpose(0, 1).unsqueeze(0)
+    k = torch.nn.functional.linear(h, k_w).view(T, n_kv, hd).transpose(0, 1).unsqueeze(0)
+    v = torch.nn.functional.linear(h, v_w).view(T, n_kv, hd).transpose(0, 1).unsqueeze(0)
+    k = k.repeat_interleave(grp, dim=1)
+    v = v.repeat_interleave(grp, dim=1)
+    a = _attention(q, k, v).squeeze(0).transpose(0, 1).reshape(T, q_w.shape[0])
     x1 = x + torch.nn.functional.linear(a, o_w)
     h2 = _rmsnorm(x1, n2)
     m = torch.nn.functional.silu(torch.nn.functional.linear(h2, g_w)) * \
@@ -380,24 +503,38 @@ def decoder_layer_fwd_bwd(p, x, n_heads, n_kv):
     y.float().square().mean().backward()
 
 
-def layout_conversion_leg(step, tokens=8192, reps=3):
-    """One GPU's share of a data-parallel step of the workload's decoder layer
-    (8K tokens per GPU, as in the pages' 70B runs): forward and backward of
-    one micro-batch, then this rank's tide_rs and tide_ag.  Beside it, the
-    layout copies TIDE removes, timed as FSDP2 makes them with torch ops:
-    the gradient pack (per-parameter bf16 -> padded rank-major fp32 buffer)
-    and the all-gather copy-out (rank-major bf16 buffer -> per-parameter
-    tensors).  Their share of the step is the analogue of the pages' 6.4%."""
-    w, plan, N, S = step.w, step.plan, step.w.world, step.plan.S
+def layer_inputs(w, tokens, seed=77):
+    """Random bf16 weights of the workload's dense decoder layer (requires
+    grad) and one micro-batch x [tokens, D]; None for other workloads."""
     if len(w.shapes) != 9:
-        return None                       # dense decoder layers only
+        return None
     D = w.shapes[0][1]
-    n_heads, n_kv = w.shapes[0][0] // 128, w.shapes[1][0] // 128
-    gen = torch.Generator(device="cuda").manual_seed(77)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
     params = [(torch.randn(s, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
               .requires_grad_() for s in w.shapes]
     x = torch.randn(tokens, D, generator=gen, device="cuda").to(torch.bfloat16)
+    return params, x, w.shapes[0][0] // 128, w.shapes[1][0] // 128
+
+
+def layout_conversion_leg(step, tokens=8192, reps=3):
+    """One GPU's share of a data-parallel step of the workload's decoder layer
+    (8K tokens per GPU, as in the pages' 70B runs): forward and backward of
+    one micro-batch, then this rank's tide_rs and tide_ag through the
+    torch.ops.tide custom operators.  Beside it, the layout copies TIDE
+    removes, timed as FSDP2 makes them with torch ops: the gradient pack
+    (per-parameter bf16 -> padded rank-major fp32 buffer) and the all-gather
+    copy-out (rank-major bf16 buffer -> per-parameter tensors).  Their share
+    of the step is the analogue of the pages' 6.4%."""
+    import parameter_layout_collectives_amd.torch_ops as tops
+
+    w, plan, N, S = step.w, step.plan, step.w.world, step.plan.S
+    li = layer_inputs(w, tokens)
+    if li is None:
+        return None                       # dense decoder layers only
+    params, x, n_heads, n_kv = li
     segs = [(plan.param(i)[0], plan.param(i)[2]) for i in range(plan.P)]
+    pid = tops.register_plan(plan)
+    grads_flat = [t for rank in step.grads for t in rank]
 
     def fwd_bwd():
         for t in params:
@@ -421,13 +558,19 @@ def layout_conversion_leg(step, tokens=8192, reps=3):
             d0, inner = (t.shape[0], t.numel() // t.shape[0])
             t.data.copy_(gb[:, off:off + seg].reshape(-1, inner)[:d0].view(t.shape))
 
+    def tide_rs_op():
+        torch.ops.tide.rs(pid, 0, grads_flat, step.blocks[0], False, False)
+
+    def tide_ag_op():
+        torch.ops.tide.ag(pid, step.gathered, step.params, False, False)
+
     fwd_bwd()
     torch.cuda.synchronize()
     assert all(t.grad is not None for t in params)
     res = {}
     for name, fn in (("fwd_bwd", fwd_bwd), ("stock_grad_pack", stock_pack),
                      ("stock_copy_out", stock_copy_out),
-                     ("tide_rs", lambda: step.rs(0)), ("tide_ag", step.ag)):
+                     ("tide_rs", tide_rs_op), ("tide_ag", tide_ag_op)):
         fn()
         ev = timed_events(reps)
         torch.cuda.synchronize()
@@ -437,17 +580,22 @@ def layout_conversion_leg(step, tokens=8192, reps=3):
             ev[k][1].record()
         torch.cuda.synchronize()
         res[name + "_ms"] = statistics.median(a.elapsed_time(b) for a, b in ev)
+    tops.unregister_plan(pid)
     copies = res["stock_grad_pack_ms"] + res["stock_copy_out_ms"]
     stock_step = res["fwd_bwd_ms"] + copies
     res.update({
         "tokens": tokens,
-        "attention_core": "elementwise stand-in (no batched bf16 products)",
+        "attention_core": "sdpa",
+        "attention_detail": "causal torch scaled_dot_product_attention (fused memory-efficient "
+                            "kernel, flash as fallback), k/v heads expanded to the query heads",
+        "tide_calls": "torch.ops.tide.rs / torch.ops.tide.ag",
         "stock_layout_copies_ms": copies,
         "stock_layout_share_pct": 100.0 * copies / stock_step,
         "tide_layout_copies_ms": 0.0,
         "tide_local_collective_share_pct":
             100.0 * (res["tide_rs_ms"] + res["tide_ag_ms"]) /
             (res["fwd_bwd_ms"] + res["tide_rs_ms"] + res["tide_ag_ms"]),
+        "pages_figure_pct": 6.4,
     })
     log(f"layout conversion: fwd+bwd {res['fwd_bwd_ms']:.2f} ms, stock copies {copies:.2f} ms "
         f"({res['stock_layout_share_pct']:.1f}% of the step), tide rs+ag "
@@ -492,30 +640,55 @@ def counter_traffic(kernel, workload, small, other_lib):
 
 
 # ---------------------------------------------------------------------------
-# co-run with a bf16 GEMM
+# co-run: a compute job on one stream, the collectives on another
 # ---------------------------------------------------------------------------
+#
+# The overlap page ("分析通信重叠", stream overlap and trace analysis) splits
+# a step into compute plus the communication time that compute does not
+# hide: T_step = T_compute + T_exposed.  Two experiments per collective and
+# launch mode measure that directly:
+#   progress  - the partner runs `reps` units (after two untimed ones)
+#               while a chain of collective calls, each with its own event
+#               pair, runs on the other stream; both start behind one gate
+#               and the chain is sized to outlast the partner.  The
+#               bytes the collective completes inside the partner's window
+#               (each call's bytes pro-rated by the share of its time spent
+#               inside) over that window give its rate beside the partner;
+#               the partner's units that ran wholly inside the chain give
+#               its slowdown.
+#   makespan  - a fixed partner chain (`reps` units) and a fixed number of
+#               collective calls (fixed_calls: the same bytes for every
+#               launch mode) start together behind one gate.  exposed =
+#               makespan - partner chain alone; serial = partner alone +
+#               collective alone; saving = serial - makespan.
 
-class Gemm:
-    """The co-running compute kernel: a bf16 GEMM on its own stream."""
+def bytes_in_window(calls, nbytes, lo, hi):
+    """Bytes a chain of calls moved inside [lo, hi] (ms): each call's
+    `nbytes` pro-rated by the share of its [start, end] inside the window."""
+    total = 0.0
+    for s, e in calls:
+        if e <= s:
+            continue
+        ov = min(e, hi) - max(s, lo)
+        if ov > 0:
+            total += nbytes * ov / (e - s)
+    return total
 
-    def __init__(self, shape, reps=30):
-        M, K, Nn = shape
-        g = torch.Generator(device="cuda").manual_seed(77)
-        self.A = torch.randn(M, K, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-        self.B = torch.randn(K, Nn, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-        self.C = torch.empty(M, Nn, dtype=torch.bfloat16, device="cuda")
-        self.flop = 2.0 * M * K * Nn
-        self.name = f"bf16 {M}x{K}x{Nn} torch.matmul"
-        self.reps = reps
-        # Two streams for the whole co-run phase: the process has few hardware
-        # queues, and a stream created later can land on the GEMM's queue,
-        # which would serialise the two instead of running them together.
-        self.stream = torch.cuda.Stream()
-        self.side = torch.cuda.Stream()
+
+class Partner:
+    """A compute job that the collectives run beside, on its own stream;
+    run() enqueues one unit of it on the current stream.  Every co-run leg
+    uses the same two streams, created once: the process has few hardware
+    queues, and a stream created later can share the partner's queue, which
+    would serialise the two instead of running them together."""
+
+    def __init__(self, name, unit, reps, streams, flop=None, kind="gemm"):
+        self.name, self.unit, self.reps, self.flop, self.kind = name, unit, reps, flop, kind
+        self.stream, self.side = streams
         torch.cuda.synchronize()
         ev = timed_events(reps)
         with torch.cuda.stream(self.stream):
-            for _ in range(5):
+            for _ in range(3):
                 self.run()
             for s, e in ev:
                 s.record()
@@ -525,16 +698,65 @@ class Gemm:
         self.alone_ms = statistics.median(s.elapsed_time(e) for s, e in ev)
 
     def run(self):
-        torch.matmul(self.A, self.B, out=self.C)
+        self.unit()
+
+    def describe(self):
+        d = {"partner": self.name, "partner_alone_ms": self.alone_ms, "partner_units": self.reps}
+        if self.flop:
+            d["partner_tflops_alone"] = self.flop / (self.alone_ms * 1e-3) / 1e12
+        return d
 
 
-def corun_chain(gemm, launch, nbytes, repeats=2):
-    """GEMMs on their stream while `launch(k, stream)` calls run back to back
-    on another stream (started first, long enough to cover every GEMM).
-    Returns the median GEMM slowdown over `repeats` runs and per-run detail;
-    only GEMMs that start and end inside the collective's window count."""
-    sb = gemm.side
-    ev = timed_events(6)
+def gemm_partner(shape, streams, reps=30):
+    """bf16 M x K x N torch.matmul (hipBLASLt), the single-wave GEMM case."""
+    M, K, Nn = shape
+    g = torch.Generator(device="cuda").manual_seed(77)
+    A = torch.randn(M, K, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    B = torch.randn(K, Nn, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    C = torch.empty(M, Nn, dtype=torch.bfloat16, device="cuda")
+    return Partner(f"bf16 {M}x{K}x{Nn} torch.matmul", lambda: torch.matmul(A, B, out=C), reps,
+                   streams, flop=2.0 * M * K * Nn)
+
+
+def layer_partner(w, streams, tokens=8192, reps=4):
+    """Forward + backward of the workload's decoder layer on one 8K-token
+    micro-batch (its own GEMMs, fused attention and elementwise kernels)."""
+    li = layer_inputs(w, tokens, seed=78)
+    if li is None:
+        return None
+    params, x, n_heads, n_kv = li
+
+    def unit():
+        for t in params:
+            t.grad = None
+        decoder_layer_fwd_bwd(params, x, n_heads, n_kv)
+
+    flop = 6.0 * tokens * w.psi
+    return Partner(f"{w.name} decoder layer forward+backward, {tokens} tokens", unit, reps,
+                   streams, flop=flop, kind="layer")
+
+
+_GATE_CYCLES = None
+
+
+def gate():
+    """Holds the current stream long enough (~25 ms) for the work enqueued
+    behind it on other streams to be queued before any of it starts."""
+    global _GATE_CYCLES
+    if _GATE_CYCLES is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(10_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _GATE_CYCLES = int(10_000_000 * 25.0 / max(a.elapsed_time(b), 1e-3))
+    torch.cuda._sleep(_GATE_CYCLES)
+
+
+def collective_alone(partner, launch, nbytes, reps=8):
+    sb = partner.side
+    ev = timed_events(reps)
     with torch.cuda.stream(sb):
         for k in range(2):
             launch(k, sb)
@@ -543,126 +765,249 @@ def corun_chain(gemm, launch, nbytes, repeats=2):
             launch(k, sb)
             e.record()
     torch.cuda.synchronize()
-    t_alone = statistics.median(s.elapsed_time(e) for s, e in ev)
+    return statistics.median(s.elapsed_time(e) for s, e in ev)
+
+
+def corun_progress(partner, launch, nbytes, t_alone, repeats=2):
+    """The progress experiment (see above); one dict per repeat."""
+    sb, cur = partner.side, torch.cuda.current_stream()
     runs = []
     for _ in range(repeats):
-        n = int(1.5 * (gemm.reps + 4) * gemm.alone_ms / t_alone) + 4
+        n = int(2.0 * (partner.reps + 2) * partner.alone_ms / t_alone) + 4
         base = torch.cuda.Event(enable_timing=True)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        first_done = torch.cuda.Event()
-        ev = timed_events(gemm.reps)
+        cev, pev = timed_events(n), timed_events(partner.reps)
         torch.cuda.synchronize()
+        # Both streams start behind one gate.  The partner is enqueued first:
+        # copy-engine calls block the host while they are queued, and the
+        # partner must not wait for that.  Its two untimed units give the
+        # chain time to get going before the timed ones.
+        gate()
         base.record()
-        sb.wait_stream(torch.cuda.current_stream())
-        gemm.stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(sb):
-            c0.record()
-            launch(0, sb)
-            first_done.record()
-            for k in range(1, n):
-                launch(k, sb)
-            c1.record()
-        with torch.cuda.stream(gemm.stream):
-            gemm.stream.wait_event(first_done)
+        sb.wait_stream(cur)
+        partner.stream.wait_stream(cur)
+        with torch.cuda.stream(partner.stream):
             for _ in range(2):
-                gemm.run()
-            for s, e in ev:
+                partner.run()
+            for s, e in pev:
                 s.record()
-                gemm.run()
+                partner.run()
+                e.record()
+        with torch.cuda.stream(sb):
+            for k, (s, e) in enumerate(cev):
+                s.record()
+                launch(k, sb)
                 e.record()
         torch.cuda.synchronize()
-        lo, hi = base.elapsed_time(c0), base.elapsed_time(c1)
-        starts = [base.elapsed_time(s) for s, _ in ev]
-        ends = [base.elapsed_time(e) for _, e in ev]
-        inside = [e - s for s, e in zip(starts, ends) if s >= lo and e <= hi]
-        if len(inside) < gemm.reps // 2:
-            log(f"co-run: only {len(inside)} of {gemm.reps} GEMMs ran inside the collective's "
-                f"window {lo:.1f}-{hi:.1f} ms (GEMMs {min(starts):.1f}-{max(ends):.1f} ms); "
-                "this run does not measure concurrency")
-            inside = []
-        med = statistics.median(inside) if inside else None
+        calls = [(base.elapsed_time(s), base.elapsed_time(e)) for s, e in cev]
+        units = [(base.elapsed_time(s), base.elapsed_time(e)) for s, e in pev]
+        c0, c1 = calls[0][0], calls[-1][1]
+        g0, g1 = units[0][0], units[-1][1]
+        inside = [e - s for s, e in units if s >= c0 and e <= c1]
+        lo, hi = max(g0, c0), min(g1, c1)
+        moved = bytes_in_window(calls, nbytes, lo, hi) if hi > lo else 0.0
+        med = statistics.median(inside) if len(inside) >= max(1, partner.reps // 2) else None
         runs.append({
-            "gemm_corun_ms": med,
-            "gemms_fully_overlapped": len(inside),
-            "gemm_slowdown_pct": None if med is None else 100.0 * (med / gemm.alone_ms - 1.0),
-            "corun_GBps": n * nbytes / ((hi - lo) * 1e-3) / 1e9,
+            "partner_unit_corun_ms": med,
+            "units_inside_chain": len(inside),
+            "partner_slowdown_pct": None if med is None else 100.0 * (med / partner.alone_ms - 1),
+            "during_partner_GBps": moved / ((hi - lo) * 1e-3) / 1e9 if hi > lo else None,
+            "partner_window_covered": c0 <= g0 and c1 >= g1,
             "calls": n,
-            "window_ms": [lo, hi],
-            "gemms_ms": [min(starts), max(ends)],
+            "chain_ms": [c0, c1],
+            "partner_ms": [g0, g1],
+            "calls_completed_in_partner_window": sum(1 for s, e in calls if s >= g0 and e <= g1),
         })
-    slow = [r["gemm_slowdown_pct"] for r in runs if r["gemm_slowdown_pct"] is not None]
-    return {
+    return runs
+
+
+def corun_makespan(partner, launch, nbytes, n, repeats=2):
+    """The makespan experiment (see above) with `n` collective calls: partner
+    chain alone, collective chain alone, both together behind one gate;
+    medians over `repeats`."""
+    sb, cur = partner.side, torch.cuda.current_stream()
+
+    def timed(do_partner, do_coll):
+        torch.cuda.synchronize()
+        gate()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        ep = ec = None
+        cev = timed_events(n) if do_coll else []
+        if do_partner:
+            partner.stream.wait_stream(cur)
+            with torch.cuda.stream(partner.stream):
+                for _ in range(partner.reps):
+                    partner.run()
+                ep = torch.cuda.Event(enable_timing=True)
+                ep.record()
+        if do_coll:
+            sb.wait_stream(cur)
+            with torch.cuda.stream(sb):
+                for k, (s, e) in enumerate(cev):
+                    s.record()
+                    launch(k, sb)
+                    e.record()
+                ec = torch.cuda.Event(enable_timing=True)
+                ec.record()
+        torch.cuda.synchronize()
+        calls = [(t0.elapsed_time(s), t0.elapsed_time(e)) for s, e in cev]
+        return (None if ep is None else t0.elapsed_time(ep),
+                None if ec is None else t0.elapsed_time(ec), calls)
+
+    rows = []
+    for _ in range(repeats):
+        tp = timed(True, False)[0]
+        tc = timed(False, True)[1]
+        tpb, tcb, calls = timed(True, True)
+        makespan = max(tpb, tcb)
+        rows.append({
+            "partner_chain_alone_ms": tp, "collective_chain_alone_ms": tc,
+            "serial_ms": tp + tc, "makespan_ms": makespan, "exposed_ms": makespan - tp,
+            "overlap_saving_ms": tp + tc - makespan,
+            "partner_chain_together_ms": tpb, "collective_chain_together_ms": tcb,
+            "during_partner_GBps_same_run":
+                bytes_in_window(calls, nbytes, 0.0, tpb) / (tpb * 1e-3) / 1e9,
+        })
+    med = {k: statistics.median(r[k] for r in rows) for k in rows[0]}
+    med.update({"collective_calls": n, "collective_bytes": n * nbytes,
+                "hidden_pct": 100.0 * med["overlap_saving_ms"] / med["collective_chain_alone_ms"],
+                "partner_slowdown_in_makespan_pct":
+                    100.0 * (med["partner_chain_together_ms"] / med["partner_chain_alone_ms"] - 1),
+                "runs": rows})
+    return med
+
+
+def fixed_calls(partner, t_ref):
+    """The collective work of the makespan experiment, the same for every
+    launch mode of one collective: beside a GEMM, calls whose time alone in
+    the default launch (t_ref ms) is half the GEMM chain's; beside the layer
+    step, one call per forward+backward (one layer's share of a step)."""
+    if partner.kind == "layer":
+        return partner.reps
+    return max(1, int(round(0.5 * partner.reps * partner.alone_ms / t_ref)))
+
+
+def corun_leg(partner, launch, nbytes, label, n_calls=None, t_alone=None):
+    """Both experiments for one collective and launch mode beside `partner`;
+    the makespan experiment runs `n_calls` calls (default: fixed_calls from
+    this mode's own time alone)."""
+    if t_alone is None:
+        t_alone = collective_alone(partner, launch, nbytes)
+    prog = corun_progress(partner, launch, nbytes, t_alone)
+    if n_calls is None:
+        n_calls = fixed_calls(partner, t_alone)
+    mk = corun_makespan(partner, launch, nbytes, n_calls)
+    slow = [r["partner_slowdown_pct"] for r in prog if r["partner_slowdown_pct"] is not None]
+    during = [r["during_partner_GBps"] for r in prog if r["during_partner_GBps"] is not None]
+    alone_gbps = nbytes / (t_alone * 1e-3) / 1e9
+    res = {
         "alone_us": t_alone * 1e3,
-        "alone_GBps": nbytes / (t_alone * 1e-3) / 1e9,
-        "corun_GBps": statistics.median(r["corun_GBps"] for r in runs),
-        "gemm_slowdown_pct": statistics.median(slow) if slow else None,
-        "runs": runs,
+        "alone_GBps": alone_gbps,
+        "partner_slowdown_pct": statistics.median(slow) if slow else None,
+        "during_partner_GBps": statistics.median(during) if during else None,
+        "progress_share_of_alone": (statistics.median(during) / alone_gbps) if during else None,
+        "serial_ms": mk["serial_ms"],
+        "makespan_ms": mk["makespan_ms"],
+        "exposed_ms": mk["exposed_ms"],
+        "overlap_saving_ms": mk["overlap_saving_ms"],
+        "hidden_pct": mk["hidden_pct"],
+        "makespan_collective_bytes": mk["collective_bytes"],
+        "partner_slowdown_in_makespan_pct": mk["partner_slowdown_in_makespan_pct"],
+        "progress_runs": prog,
+        "makespan": mk,
     }
-
-
-CORUN_METHOD = ("stream A runs the GEMMs, stream B a chain of collective calls started first and "
-                "long enough to cover them; slowdown = median GEMM time while the chain runs / "
-                "median GEMM time alone - 1, counting only GEMMs that start and end inside the "
-                "chain's window; median of 2 runs")
-
-
-def corun_rs(w, gemm):
-    """tide_rs beside the GEMM, default and small-footprint launch."""
-    N = w.world
-    log(f"co-run: generating {w.name} ({N} ranks) beside a {gemm.name}")
-    grads = workloads.all_grads(w, device="cuda")
-    plan = tide.Plan(w.shapes, N)
-    table = tide.grad_table(plan, grads)
-    out = torch.empty(N, plan.S, dtype=torch.float32, device="cuda")
-    b_rs = rs_bytes(plan, 0)
-    res = {"gemm": gemm.name, "gemm_alone_ms": gemm.alone_ms,
-           "gemm_tflops_alone": gemm.flop / (gemm.alone_ms * 1e-3) / 1e12,
-           "workload": w.name, "world": N, "method": CORUN_METHOD}
-    for small in (False, True):
-        key = "small_footprint" if small else "default"
-        r = corun_chain(gemm, lambda k, st: tide.rs(plan, k % N, table, out[k % N], small=small,
-                                                     stream=st), b_rs)
-        res[key] = {"tide_rs_alone_us": r["alone_us"], "tide_rs_alone_GBps": r["alone_GBps"],
-                    "tide_rs_corun_GBps": r["corun_GBps"],
-                    "gemm_slowdown_pct": r["gemm_slowdown_pct"], "runs": r["runs"]}
-        log(f"co-run tide_rs {key}: slowdown {fmt(r['gemm_slowdown_pct'])}% runs {r['runs']}, "
-            f"{r['corun_GBps']:.0f} GB/s during, {r['alone_GBps']:.0f} GB/s alone")
-    del grads, table, out
+    log(f"co-run {label}: partner slowdown {fmt(res['partner_slowdown_pct'])}%, "
+        f"{fmt(res['during_partner_GBps'])} GB/s during the partner "
+        f"({fmt(res['alone_GBps'])} alone); {n_calls} calls: serial {mk['serial_ms']:.2f} ms, "
+        f"makespan {mk['makespan_ms']:.2f} ms, exposed {mk['exposed_ms']:.2f} ms "
+        f"({mk['hidden_pct']:.0f}% of the collective hidden)")
     return res
 
 
-def corun_rs_step(step, gemm):
-    """tide_rs beside the GEMM on the step's workload (its gradients are
-    already resident), default and small-footprint launch."""
-    plan, N = step.plan, step.w.world
-    res = {"gemm": gemm.name, "gemm_alone_ms": gemm.alone_ms, "workload": step.w.name,
-           "world": N, "method": CORUN_METHOD}
-    for small in (False, True):
-        key = "small_footprint" if small else "default"
-        r = corun_chain(gemm, lambda k, st: tide.rs(plan, k % N, step.table, step.blocks[k % N],
-                                                     small=small, stream=st), step.b_rs)
-        res[key] = {"tide_rs_alone_us": r["alone_us"], "tide_rs_alone_GBps": r["alone_GBps"],
-                    "tide_rs_corun_GBps": r["corun_GBps"],
-                    "gemm_slowdown_pct": r["gemm_slowdown_pct"], "runs": r["runs"]}
-        log(f"co-run tide_rs ({step.w.name}) {key}: slowdown {fmt(r['gemm_slowdown_pct'])}%, "
-            f"{r['corun_GBps']:.0f} GB/s during, {r['alone_GBps']:.0f} GB/s alone")
+CORUN_METHOD = (
+    "progress: the partner's units run while a longer chain of collective calls (an event pair "
+    "per call) runs on the other stream; during_partner_GBps = bytes completed inside the "
+    "partner's window (calls pro-rated by their share inside) / that window; slowdown = median "
+    "unit time inside the chain / median unit time alone - 1 (median of 2 runs). makespan: a "
+    "fixed partner chain and a fixed number of collective calls, the same for every launch mode "
+    "(beside a GEMM: calls whose default-launch time alone is half the GEMM chain's; beside the "
+    "layer step: one call per forward+backward), start together behind one gate; exposed = "
+    "makespan - partner chain alone, serial = sum of the two alone, saving = serial - makespan "
+    "(median of 2 runs)")
+
+
+def _with_keys(partner_kind, leg):
+    """Names the partner in the rate key: during_gemm_GBps beside a GEMM,
+    during_step_GBps beside the layer step."""
+    key = "during_gemm_GBps" if partner_kind == "gemm" else "during_step_GBps"
+    slow = "gemm_slowdown_pct" if partner_kind == "gemm" else "step_slowdown_pct"
+    leg[key] = leg["during_partner_GBps"]
+    leg[slow] = leg["partner_slowdown_pct"]
+    return leg
+
+
+def corun_modes(grids, copy_engine):
+    """(name, launch keywords) of the co-run launch modes: default, small
+    footprint, small footprint on a persistent grid of g workgroups for each
+    g in `grids` (max_workgroups = g: each workgroup loops over tiles), and
+    the copy engines (tide_ag)."""
+    modes = [("default", {}), ("small_footprint", {"small": True})]
+    modes += [(f"small_footprint_wg{g}", {"small": True, "max_workgroups": g}) for g in grids]
+    if copy_engine:
+        modes.append(("copy_engine", {"copy_engine": True}))
+    return modes
+
+
+def corun_rs(partner, kind, w=None, step=None, grids=()):
+    """tide_rs beside `partner` in each launch mode of corun_modes, on the
+    step's resident workload or on workload `w` (generated here)."""
+    if step is not None:
+        plan, table, out, N, name = step.plan, step.table, step.blocks, step.w.world, step.w.name
+        b_rs = step.b_rs
+    else:
+        N, name = w.world, w.name
+        log(f"co-run: generating {name} ({N} ranks) beside {partner.name}")
+        grads = workloads.all_grads(w, device="cuda")
+        plan = tide.Plan(w.shapes, N)
+        table = tide.grad_table(plan, grads)
+        out = torch.empty(N, plan.S, dtype=torch.float32, device="cuda")
+        b_rs = rs_bytes(plan, 0)
+    res = dict(partner.describe(), workload=name, world=N, bytes_per_call=b_rs,
+               method=CORUN_METHOD)
+    n_calls = None
+    for key, kw in corun_modes(grids, copy_engine=False):
+
+        def launch(k, st, kw=kw):
+            tide.rs(plan, k % N, table, out[k % N], stream=st, **kw)
+
+        t_alone = collective_alone(partner, launch, b_rs)
+        if n_calls is None:   # the default launch's time sets the work for every mode
+            n_calls = fixed_calls(partner, t_alone)
+        res[key] = _with_keys(kind, corun_leg(partner, launch, b_rs,
+                                              f"tide_rs {name} {key} beside {partner.name}",
+                                              n_calls=n_calls, t_alone=t_alone))
+    if step is None:
+        del grads, table, out
     return res
 
 
-def corun_ag(step, gemm):
-    """tide_ag beside the GEMM: kernel (default, small footprint) and SDMA copy engine."""
-    res = {"gemm": gemm.name, "gemm_alone_ms": gemm.alone_ms, "workload": step.w.name,
-           "world": step.w.world, "method": CORUN_METHOD}
-    for key, kw in (("default", {}), ("small_footprint", {"small": True}),
-                    ("copy_engine", {"copy_engine": True})):
-        r = corun_chain(gemm, lambda k, st: tide.ag(step.plan, None, None, stream=st,
-                                                     tables=step.agt, **kw), step.b_ag)
-        res[key] = {"tide_ag_alone_us": r["alone_us"], "tide_ag_alone_GBps": r["alone_GBps"],
-                    "tide_ag_corun_GBps": r["corun_GBps"],
-                    "gemm_slowdown_pct": r["gemm_slowdown_pct"], "runs": r["runs"]}
-        log(f"co-run tide_ag {key}: slowdown {fmt(r['gemm_slowdown_pct'])}% runs {r['runs']}, "
-            f"{r['corun_GBps']:.0f} GB/s during, {r['alone_GBps']:.0f} GB/s alone")
+def corun_ag(partner, kind, step, grids=()):
+    """tide_ag beside `partner` in each launch mode of corun_modes, the SDMA
+    copy engines included."""
+    res = dict(partner.describe(), workload=step.w.name, world=step.w.world,
+               bytes_per_call=step.b_ag, method=CORUN_METHOD)
+    n_calls = None
+    for key, kw in corun_modes(grids, copy_engine=True):
+
+        def launch(k, st, kw=kw):
+            tide.ag(step.plan, None, None, stream=st, tables=step.agt, **kw)
+
+        t_alone = collective_alone(partner, launch, step.b_ag)
+        if n_calls is None:
+            n_calls = fixed_calls(partner, t_alone)
+        res[key] = _with_keys(kind, corun_leg(
+            partner, launch, step.b_ag, f"tide_ag {step.w.name} {key} beside {partner.name}",
+            n_calls=n_calls, t_alone=t_alone))
     return res
 
 
@@ -700,9 +1045,10 @@ def cpu_baseline(step, min_reps=3, max_reps=40, budget_s=10.0):
         t2 = time.perf_counter()
         t_rs.append(t1 - t0)
         t_ag.append(t2 - t1)
-        if k < 3:
-            log(f"cpu baseline rep {k}: rs {t1 - t0:.3f} s, ag {t2 - t1:.3f} s")
     trs, tag = statistics.median(t_rs), statistics.median(t_ag)
+    log(f"cpu baseline over {len(t_rs)} reps: rs min/median/max {min(t_rs):.3f}/{trs:.3f}/"
+        f"{max(t_rs):.3f} s, ag {min(t_ag):.3f}/{tag:.3f}/{max(t_ag):.3f} s; per rep rs "
+        + " ".join(f"{x:.3f}" for x in t_rs) + "; ag " + " ".join(f"{x:.3f}" for x in t_ag))
     # the tiny workload on one thread (latency, not bandwidth)
     tw = workloads.WORKLOADS["tiny"]
     tg = [[workloads.bf16_bits(t).reshape(-1) for t in rank] for rank in workloads.all_grads(tw)]
@@ -737,12 +1083,43 @@ def cpu_baseline(step, min_reps=3, max_reps=40, budget_s=10.0):
                    f"median of {len(t_rs)} repetitions (~{budget_s:.0f} s); host copies not timed"),
         "rs_s": trs,
         "ag_s": tag,
+        "rs_s_min_median_max": [min(t_rs), trs, max(t_rs)],
+        "ag_s_min_median_max": [min(t_ag), tag, max(t_ag)],
+        "reps": len(t_rs),
         "tiny_step_us_1_thread": statistics.median(t_tiny) * 1e6,
         "cpu_model": cpu,
     }
 
 
 # ---------------------------------------------------------------------------
+
+LEGS = ("variants", "small_alone", "tiny", "two_stage", "layout", "copy", "cpu", "corun_gemm",
+        "corun_layer", "corun_n64", "partner_gemm")
+
+
+def corun_summary(results):
+    """One row per (collective, workload, partner, mode) of the co-run legs."""
+    rows = []
+    for coll, res in results:
+        if not res:
+            continue
+        for mode, leg in res.items():
+            if not isinstance(leg, dict) or "exposed_ms" not in leg:
+                continue
+            rows.append({
+                "collective": coll, "workload": res["workload"], "partner": res["partner"],
+                "mode": mode,
+                "partner_slowdown_pct": leg["partner_slowdown_pct"],
+                "during_partner_GBps": leg["during_partner_GBps"],
+                "alone_GBps": leg["alone_GBps"],
+                "progress_share_of_alone": leg["progress_share_of_alone"],
+                "serial_ms": leg["serial_ms"], "makespan_ms": leg["makespan_ms"],
+                "exposed_ms": leg["exposed_ms"], "hidden_pct": leg["hidden_pct"],
+                "makespan_collective_bytes": leg.get("makespan_collective_bytes"),
+                "partner_slowdown_in_makespan_pct": leg.get("partner_slowdown_in_makespan_pct"),
+            })
+    return rows
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -764,9 +1141,30 @@ def main():
                     help="load the libtide.so at this path instead of the in-tree one (e.g. one "
                          "built with other tuning macros)")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the tide_rs flag variants (bf16 shard, mean) and the "
-                         "two-stage reduce-scatter")
+                    help="skip the tide_rs flag variants (bf16 shard, mean), the small-footprint "
+                         "alone timing, the tiny workload, the two-stage reduce-scatter and the "
+                         "layout-conversion leg")
+    ap.add_argument("--corun-grids", default="128",
+                    help="comma-separated persistent grid sizes (max_workgroups) for extra "
+                         "small-footprint co-run modes, or 'none'")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated subset of the sections after the step: "
+                         + ",".join(LEGS) + " (default: all)")
     args = ap.parse_args()
+    grids = () if args.corun_grids == "none" else tuple(
+        int(g) for g in args.corun_grids.split(",") if g)
+    legs = set(LEGS) if args.legs == "all" else set(args.legs.split(","))
+    unknown = legs - set(LEGS)
+    if unknown:
+        ap.error(f"--legs: unknown {sorted(unknown)}; choose from {','.join(LEGS)}")
+    if args.no_variants:
+        legs -= {"variants", "small_alone", "tiny", "two_stage", "layout"}
+    if args.no_cpu:
+        legs.discard("cpu")
+    if args.no_copy:
+        legs.discard("copy")
+    if args.corun == "none":
+        legs -= {"corun_gemm", "corun_layer", "corun_n64", "partner_gemm"}
 
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (--gpus {args.gpus} requested); "
@@ -811,31 +1209,49 @@ def main():
         "mean_launch_us": dom["mean_us"],
     }
 
-    variants = None if args.no_variants else rs_variants(step)
-    small_alone = None if args.no_variants else small_footprint_alone(step)
-    tiny = None if args.no_variants else tiny_latency()
-    two_stage = None if args.no_variants else two_stage_leg(step)
-    layout = None if args.no_variants else layout_conversion_leg(step)
-    copy_gbps, copy_lib_gbps = (None, None) if args.no_copy else \
-        copy_ceiling(library=not args.no_lib_copy)
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())   # every two-stream leg uses these
+    variants = rs_variants(step) if "variants" in legs else None
+    small_alone = small_footprint_alone(step) if "small_alone" in legs else None
+    tiny = tiny_latency() if "tiny" in legs else None
+    two_stage = two_stage_leg(step, streams) if "two_stage" in legs else None
+    layout = layout_conversion_leg(step) if "layout" in legs else None
+    copy_gbps, copy_lib_gbps = copy_ceiling(library=not args.no_lib_copy) if "copy" in legs \
+        else (None, None)
     if copy_gbps:
         log(f"copy ceiling {copy_gbps:.1f} GB/s (torch), {fmt(copy_lib_gbps)} GB/s (library)")
-    cpu = None if args.no_cpu else cpu_baseline(step)
-    corun_res = corun_ag_res = corun_rs_step_res = None
+    cpu = cpu_baseline(step) if "cpu" in legs else None
+    corun_res = corun_ag_res = corun_rs_step_res = corun_layer_res = None
     gemm = None
-    if args.corun != "none":
-        cw = workloads.WORKLOADS[args.corun]
-        gemm = Gemm(cw.corun_gemm or (8192, 8192, 8192))
-        corun_ag_res = corun_ag(step, gemm)
-        corun_rs_step_res = corun_rs_step(step, gemm)
+    cw = workloads.WORKLOADS[args.corun] if args.corun != "none" else None
+    if legs & {"corun_gemm", "corun_n64"}:
+        gemm = gemm_partner(cw.corun_gemm or (8192, 8192, 8192), streams)
+        log(f"partner: {gemm.name}, {gemm.alone_ms:.3f} ms alone")
+    if "corun_gemm" in legs:
+        corun_ag_res = corun_ag(gemm, "gemm", step, grids)
+        corun_rs_step_res = corun_rs(gemm, "gemm", step=step, grids=grids)
+    if "corun_layer" in legs:
+        layer = layer_partner(step.w, streams)
+        if layer is not None:
+            log(f"partner: {layer.name}, {layer.alone_ms:.2f} ms alone")
+            corun_layer_res = {"tide_rs": corun_rs(layer, "layer", step=step, grids=grids),
+                               "tide_ag": corun_ag(layer, "layer", step, grids)}
+            del layer
+    if "partner_gemm" in legs and gemm is None:
+        gemm = gemm_partner(cw.corun_gemm or (8192, 8192, 8192), streams)
+        log(f"partner: {gemm.name}, {gemm.alone_ms:.3f} ms alone")
     P, S = step.plan.P, step.plan.S
     del step
     gc.collect()
     torch.cuda.empty_cache()
-    if gemm is not None:
-        corun_res = corun_rs(cw, gemm)
+    if "corun_n64" in legs:
+        corun_res = corun_rs(gemm, "gemm", w=cw, grids=grids)
         gc.collect()
         torch.cuda.empty_cache()
+    summary = corun_summary([("tide_rs", corun_res), ("tide_ag", corun_ag_res),
+                             ("tide_rs", corun_rs_step_res)] +
+                            ([("tide_rs", corun_layer_res["tide_rs"]),
+                              ("tide_ag", corun_layer_res["tide_ag"])] if corun_layer_res
+                             else []))
 
     line = {
         "metric": "tide_rs/tide_ag effective HBM GB/s + % of peak; co-run GEMM slowdown %",
@@ -880,6 +1296,9 @@ def main():
         "corun": corun_res,
         "corun_ag": corun_ag_res,
         "corun_rs_step_workload": corun_rs_step_res,
+        "corun_layer_step": corun_layer_res,
+        "corun_summary": summary,
+        "corun_partner_gemm": gemm.describe() if gemm is not None else None,
         "gemm_slowdown_pct": None if not corun_res else {
             k: corun_res[k]["gemm_slowdown_pct"] for k in ("default", "small_footprint")
             if k in corun_res},

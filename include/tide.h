@@ -88,20 +88,28 @@ typedef struct tide_plan tide_plan;
 /* Launch flag: small-footprint mode, for running beside a compute kernel on
  * another stream (e.g. a bf16 GEMM).  Every tile still gets a short-lived
  * workgroup, but each one reserves just over half of a compute unit's LDS,
- * so at most one is resident per compute unit at any moment and the other
- * kernel keeps its place on every unit.  The pages trace the interference to
- * collectives that occupy the compute units a concurrent GEMM needs (TIDE
- * article, §"FSDP2通信开销的根源"); TIDE's answer is to keep collectives off
- * them, with copy engines and short-lived thread blocks (§"TIDE的设计思路"). */
+ * so at most one is resident per compute unit at any moment, and it holds
+ * that unit for one tile only.  A compute kernel that fills every unit
+ * waits at most one tile for a unit; beside such a kernel (a single-wave
+ * GEMM) the collective makes progress mainly in the kernel's launch gaps and
+ * tail.  The pages trace the interference to collectives that occupy the
+ * compute units a concurrent GEMM needs (TIDE article, §"FSDP2通信开销的根源");
+ * TIDE's answer is to keep collectives off them, with copy engines and
+ * short-lived thread blocks (§"TIDE的设计思路").  max_workgroups > 0 with
+ * this flag runs a persistent grid instead: more progress beside a compute
+ * kernel, which then loses the units that grid holds. */
 #define TIDE_F_SMALL_FOOTPRINT 0x1u
 
 /* Launch flag, tide_ag only: place the shards with the SDMA copy engines
- * (hipMemcpyDeviceToDeviceNoCU copies) and no kernel at all, so a concurrent
- * compute kernel keeps every compute unit.  This is the analogue of TIDE-AG
- * moving data without occupying SMs (TIDE article, §"TIDE的设计思路").  One
- * 2-D copy per parameter covers the ranks that hold full shards when the N
- * rank blocks are equally spaced; otherwise one copy per (parameter, rank).
- * tide_rs rejects it with TIDE_E_UNSUPPORTED: a reduction needs arithmetic. */
+ * (hipMemcpyDeviceToDeviceNoCU copies) and no kernel of the library's own,
+ * so a concurrent compute kernel keeps the compute units.  This is the
+ * analogue of TIDE-AG moving data without occupying SMs (TIDE article,
+ * §"TIDE的设计思路").  One 1-D copy per (parameter, rank) run with real
+ * elements: P*N copies at most, each costing some tens of microseconds of
+ * host time to enqueue (the call returns when all are queued).  The HIP
+ * runtime itself may still move copies of about a kilobyte or less with a
+ * small kernel.  tide_rs rejects the flag with TIDE_E_UNSUPPORTED: a
+ * reduction needs arithmetic. */
 #define TIDE_F_COPY_ENGINE 0x2u
 
 /* Flags, tide_rs only: the gradient element type.  Without either flag the

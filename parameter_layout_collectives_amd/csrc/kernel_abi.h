@@ -85,8 +85,9 @@ struct Tile {
 #define TIDE_SMALL_AG_U 4
 #endif
 // Small-footprint copies (all-gather placement, pack): one 1024-lane
-// workgroup per CU.  Its 16 light waves (few VGPRs, no ALU work) fit beside
-// a GEMM's resident waves and keep many bytes in flight.
+// workgroup per CU.  Its 16 light waves (few VGPRs, no ALU work) keep many
+// bytes in flight, so each workgroup finishes its tile, and frees its CU,
+// quickly.
 #ifndef TIDE_SMALL_AG_BLOCK
 #define TIDE_SMALL_AG_BLOCK 1024
 #endif

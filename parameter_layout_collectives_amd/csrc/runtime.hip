@@ -42,10 +42,10 @@ namespace {
 // Small-footprint TIDE-RS for at most this many ranks runs the default
 // kernel shape (4 chunks per lane over 4096-element tiles) under the
 // small-footprint LDS reservation; for more ranks, the lighter small shape
-// (2 chunks per lane, 2048-element tiles, 16-rank batches).  Beside a bf16
-// 8192^3 GEMM the default shape moved 37% (8 ranks) and 20% (16 ranks)
-// more bytes than the small one at 0.3% and 3.5% GEMM slowdown, but at 64
-// ranks it cost the GEMM 9.9% against the small shape's 4.6-7.1%.
+// (2 chunks per lane, 2048-element tiles, 16-rank batches), whose shorter
+// workgroups hand CUs back sooner.  Beside a bf16 8192^3 GEMM the default
+// shape cost the GEMM 0.3% (8 ranks) and 3.5% (16 ranks), but 9.9% at 64
+// ranks against the small shape's 4.6-7.1%.
 #ifndef TIDE_SMALL_FEW_RANKS
 #define TIDE_SMALL_FEW_RANKS 16
 #endif
@@ -430,9 +430,12 @@ RsPolicy rs_policy(const DeviceLimits &lim, int32_t N, uint32_t flags) {
 // Both launch modes give every tile its own short-lived workgroup, and the
 // hardware dispatcher balances them over all CUs.  Small-footprint launches
 // also reserve over half a CU's LDS per workgroup, so at most one of them
-// is resident on a CU at any moment: a concurrent GEMM keeps its place on
-// every CU and loses only a little issue bandwidth there.  max_wg > 0 caps
-// the grid (workgroups then loop over tiles).
+// is resident on a CU at any moment, and each holds its CU for one tile
+// only.  A kernel that fills every CU (a single-wave GEMM) does not place a
+// workgroup on a CU that holds one of ours, so beside it these workgroups
+// run in its launch gaps and tail, and it waits at most one tile for a CU.
+// max_wg > 0 caps the grid (workgroups then loop over tiles and keep their
+// CUs for the whole call).
 unsigned grid_size(const DeviceLimits &lim, int64_t ntiles, uint32_t flags, int32_t max_wg) {
     int64_t g;
     if (flags & TIDE_F_SMALL_FOOTPRINT)
@@ -524,57 +527,31 @@ namespace tide {
 namespace {
 
 // TIDE-AG placement with the SDMA engines: the same (parameter, rank) runs as
-// the kernel copies, as device-to-device copies that use no compute unit.
-// The ranks holding a full shard of parameter i form a prefix 0..F-1; when
-// the rank blocks are equally spaced (one gathered buffer) those F runs are
-// one 2-D copy: F rows of seg_i elements, source pitch = block spacing,
-// destination pitch = seg_i.  The one short rank (if any) is a 1-D copy.
+// the kernel copies, each as one device-to-device copy of the no-CU kind,
+// which the HIP runtime hands to an SDMA engine.  Only 1-D copies: a 2-D
+// copy of that kind runs as a blit kernel on the compute units (a kernel
+// trace of it shows one copyBufferRect kernel per parameter), which is what
+// this path exists to avoid.  The runtime still moves very small copies
+// (around a kilobyte) with a kernel.  Each copy costs tens of microseconds
+// of host time to enqueue, so the call returns once all P*N copies are
+// queued.
 tide_status ag_copy_engine(const tide_plan *p, const void *const *rank_src, void *const *params,
                            int32_t e, hipStream_t stream) {
     const hipMemcpyKind kind = hipMemcpyDeviceToDeviceNoCU;
     const uintptr_t eb = static_cast<uintptr_t>(e);
-    bool equal = p->N > 1;
-    uintptr_t pitch = 0;
-    if (equal) {
-        const uintptr_t b0 = reinterpret_cast<uintptr_t>(rank_src[0]);
-        const uintptr_t b1 = reinterpret_cast<uintptr_t>(rank_src[1]);
-        equal = b1 > b0;
-        pitch = b1 - b0;
-        for (int32_t r = 2; equal && r < p->N; r++)
-            equal = reinterpret_cast<uintptr_t>(rank_src[r]) ==
-                    reinterpret_cast<uintptr_t>(rank_src[r - 1]) + pitch;
-    }
     for (int32_t i = 0; i < p->P; i++) {
         if (p->numel[i] == 0 || p->seg[i] == 0) continue;
-        const uintptr_t seg_b = static_cast<uintptr_t>(p->seg[i]) * eb;
         const uintptr_t off_b = static_cast<uintptr_t>(p->off[i]) * eb;
         char *dst = static_cast<char *>(params[i]);
-        int32_t full = 0;
-        while (full < p->N) {
+        for (int32_t r = 0; r < p->N; r++) {
             int64_t src, L;
-            shard_run(p, full, i, &src, &L);
-            if (L != p->seg[i]) break;
-            full++;
+            shard_run(p, r, i, &src, &L);
+            if (L == 0) break;   // the ranks after a short or empty shard hold nothing
+            hipError_t err = hipMemcpyAsync(dst + static_cast<uintptr_t>(src) * eb,
+                                            static_cast<const char *>(rank_src[r]) + off_b,
+                                            static_cast<uintptr_t>(L) * eb, kind, stream);
+            if (err != hipSuccess) return hip_fail("tide_ag: copy-engine copy", err);
         }
-        hipError_t err = hipSuccess;
-        if (equal && full > 1 && pitch >= seg_b) {
-            err = hipMemcpy2DAsync(dst, seg_b, static_cast<const char *>(rank_src[0]) + off_b,
-                                   pitch, seg_b, static_cast<size_t>(full), kind, stream);
-        } else {
-            for (int32_t r = 0; r < full && err == hipSuccess; r++)
-                err = hipMemcpyAsync(dst + static_cast<uintptr_t>(r) * seg_b,
-                                     static_cast<const char *>(rank_src[r]) + off_b, seg_b, kind,
-                                     stream);
-        }
-        if (err == hipSuccess && full < p->N) {
-            int64_t src, L;
-            shard_run(p, full, i, &src, &L);
-            if (L > 0)
-                err = hipMemcpyAsync(dst + static_cast<uintptr_t>(src) * eb,
-                                     static_cast<const char *>(rank_src[full]) + off_b,
-                                     static_cast<uintptr_t>(L) * eb, kind, stream);
-        }
-        if (err != hipSuccess) return hip_fail("tide_ag: copy-engine copy", err);
     }
     return TIDE_OK;
 }

@@ -61,3 +61,30 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_bytes_in_window_prorates_straddling_calls():
+    calls = [(0.0, 1.0), (1.0, 3.0), (3.0, 4.0)]
+    # window [0.5, 3.5] ms: half of the first call, all of the second, half
+    # of the third
+    assert bench.bytes_in_window(calls, 100, 0.5, 3.5) == 50 + 100 + 50
+    assert bench.bytes_in_window(calls, 100, 1.0, 3.0) == 100
+    assert bench.bytes_in_window(calls, 100, 5.0, 6.0) == 0
+    assert bench.bytes_in_window([(2.0, 2.0)], 100, 0.0, 5.0) == 0
+
+
+def test_corun_summary_rows():
+    leg = {"partner_slowdown_pct": 5.0, "during_partner_GBps": 1000.0, "alone_GBps": 5000.0,
+           "progress_share_of_alone": 0.2, "serial_ms": 10.0, "makespan_ms": 8.0,
+           "exposed_ms": 2.0, "hidden_pct": 40.0}
+    res = {"workload": "w", "partner": "p", "default": leg, "small_footprint": leg}
+    rows = bench.corun_summary([("tide_rs", res), ("tide_ag", None)])
+    assert [r["mode"] for r in rows] == ["default", "small_footprint"]
+    assert rows[0]["exposed_ms"] == 2.0 and rows[0]["collective"] == "tide_rs"
+
+
+def test_unknown_leg_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--legs", "bogus"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "unknown" in r.stderr
