@@ -604,6 +604,56 @@ def layout_conversion_leg(step, tokens=8192, reps=3):
     return res
 
 
+def fit_leg(w, repeats=(1, 4), reps=20, warmup=3):
+    """Per-launch fixed cost and in-kernel rate of tide_rs and tide_ag on the
+    workload's shapes: each call is timed on a bucket of K copies of the
+    layer (K in `repeats`, separate gradients and buffers for every copy, so
+    nothing is re-read from a cache), and t = t0 + B / r is fitted through
+    the two (B, t) points."""
+    res = {"workload": w.name, "repeats": list(repeats)}
+    pts = {"tide_rs": [], "tide_ag": []}
+    for K in repeats:
+        wk = dataclasses.replace(w, name=f"{w.name}_x{K}",
+                                 params=[(f"{n}#{k}", s) for k in range(K) for n, s in w.params])
+        grads = workloads.all_grads(wk, device="cuda")
+        plan = tide.Plan(wk.shapes, wk.world)
+        table = tide.grad_table(plan, grads)
+        N = wk.world
+        out = torch.empty(N, plan.S, dtype=torch.float32, device="cuda")
+        gathered = workloads.random_bf16(N * plan.S, seed=4242, sigma=w.sigma, device="cuda")
+        params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in wk.shapes]
+        agt = tide.ag_tables(plan, gathered, params)
+        for name, fn, nbytes in (
+                ("tide_rs", lambda k: tide.rs(plan, k % N, table, out[k % N]), rs_bytes(plan, 0)),
+                ("tide_ag", lambda k: tide.ag(plan, None, None, tables=agt), ag_bytes(plan))):
+            for k in range(warmup):
+                fn(k)
+            ev = timed_events(reps)
+            torch.cuda.synchronize()
+            for k in range(reps):
+                ev[k][0].record()
+                fn(k)
+                ev[k][1].record()
+            torch.cuda.synchronize()
+            t = statistics.fmean(a.elapsed_time(b) for a, b in ev) * 1e3   # us
+            pts[name].append((nbytes, t))
+            log(f"fit: {name} x{K}: {nbytes / 1e9:.3f} GB in {t:.1f} us "
+                f"({nbytes / t / 1e3:.0f} GB/s)")
+        del grads, table, out, gathered, params, agt
+        gc.collect()
+        torch.cuda.empty_cache()
+    for name, p in pts.items():
+        (b1, t1), (b2, t2) = p[0], p[-1]
+        r = (b2 - b1) / (t2 - t1) / 1e3          # GB/s
+        t0 = t1 - b1 / (r * 1e3)
+        res[name] = {"points_bytes_us": p, "fixed_us": t0, "in_kernel_GBps": r,
+                     "in_kernel_pct_of_peak": 100.0 * r / HBM_PEAK_GBPS,
+                     "single_GBps": b1 / t1 / 1e3}
+        log(f"fit: {name}: fixed cost {t0:.1f} us per launch, in-kernel {r:.0f} GB/s "
+            f"({100 * r / HBM_PEAK_GBPS:.1f}% of peak)")
+    return res
+
+
 def kernel_stats(name, nbytes, times):
     mean = statistics.fmean(times)
     q = sorted(times)
@@ -1094,7 +1144,7 @@ def cpu_baseline(step, min_reps=3, max_reps=40, budget_s=10.0):
 # ---------------------------------------------------------------------------
 
 LEGS = ("variants", "small_alone", "tiny", "two_stage", "layout", "copy", "cpu", "corun_gemm",
-        "corun_layer", "corun_n64", "partner_gemm")
+        "corun_layer", "corun_n64", "partner_gemm", "fit")
 
 
 def corun_summary(results):
@@ -1149,11 +1199,13 @@ def main():
                          "small-footprint co-run modes, or 'none'")
     ap.add_argument("--legs", default="all",
                     help="comma-separated subset of the sections after the step: "
-                         + ",".join(LEGS) + " (default: all)")
+                         + ",".join(LEGS) + "; 'all' (the default) is every one but fit; "
+                         "'none' runs the step only")
     args = ap.parse_args()
     grids = () if args.corun_grids == "none" else tuple(
         int(g) for g in args.corun_grids.split(",") if g)
-    legs = set(LEGS) if args.legs == "all" else set(args.legs.split(","))
+    legs = set(LEGS) - {"fit"} if args.legs == "all" else \
+        set() if args.legs == "none" else set(args.legs.split(","))
     unknown = legs - set(LEGS)
     if unknown:
         ap.error(f"--legs: unknown {sorted(unknown)}; choose from {','.join(LEGS)}")
@@ -1220,6 +1272,7 @@ def main():
     if copy_gbps:
         log(f"copy ceiling {copy_gbps:.1f} GB/s (torch), {fmt(copy_lib_gbps)} GB/s (library)")
     cpu = cpu_baseline(step) if "cpu" in legs else None
+    fit = None
     corun_res = corun_ag_res = corun_rs_step_res = corun_layer_res = None
     gemm = None
     cw = workloads.WORKLOADS[args.corun] if args.corun != "none" else None
@@ -1247,6 +1300,8 @@ def main():
         corun_res = corun_rs(gemm, "gemm", w=cw, grids=grids)
         gc.collect()
         torch.cuda.empty_cache()
+    if "fit" in legs:
+        fit = fit_leg(w)
     summary = corun_summary([("tide_rs", corun_res), ("tide_ag", corun_ag_res),
                              ("tide_rs", corun_rs_step_res)] +
                             ([("tide_rs", corun_layer_res["tide_rs"]),
@@ -1299,6 +1354,7 @@ def main():
         "corun_layer_step": corun_layer_res,
         "corun_summary": summary,
         "corun_partner_gemm": gemm.describe() if gemm is not None else None,
+        "fixed_cost_fit": fit,
         "gemm_slowdown_pct": None if not corun_res else {
             k: corun_res[k]["gemm_slowdown_pct"] for k in ("default", "small_footprint")
             if k in corun_res},
