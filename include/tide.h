@@ -52,7 +52,9 @@
  * costs a hash and a compare on the host and no upload; a new set is copied
  * through a pinned staging buffer by an async copy on the call's stream.
  * Replacing a set waits (on the host) until the launches that read it have
- * finished.  A call on another stream that hits a set whose upload may still
+ * finished, through one event per stream that read it (up to 16 streams per
+ * cached set; a further stream takes over the entry of one whose reads have
+ * finished), never through a device-wide synchronisation.  A call on another stream that hits a set whose upload may still
  * be in flight makes its stream wait for that upload.
  *
  * Graph capture.  tide_rs, tide_ag, tide_pack and tide_rs_slots may be
@@ -149,8 +151,10 @@ tide_status tide_plan_create(int32_t world, int32_t nparams, const int64_t *dim0
                              const int64_t *inner, int64_t align_elems,
                              tide_plan **out_plan);
 
-/* Release a plan.  Waits for the devices the plan was used on to go idle
- * before freeing its device tables.  NULL is ignored. */
+/* Release a plan.  Before freeing its device tables it waits for the launches
+ * that may read them (an event per stream that used the plan); if a graph
+ * captured a launch of the plan, it waits for the whole device instead.
+ * NULL is ignored. */
 void tide_plan_destroy(tide_plan *plan);
 
 int32_t tide_plan_world(const tide_plan *plan);          /* N, or -1 if plan is NULL */

@@ -19,15 +19,20 @@ namespace tide {
 // are allocated once and reused for every pointer set it holds: a new set
 // is written to the pinned staging copy and uploaded with an async copy on
 // the caller's stream, so the launch that follows reads it in stream order.
+// A stream that has read a slot, and the event recorded on it after its
+// latest read (upload or launch).
+struct SlotReader {
+    void *stream;                // hipStream_t
+    void *event;                 // hipEvent_t, owned by the slot
+};
+
 struct PtrTable {
     std::vector<uintptr_t> key;  // the host pointer array it was built from
     uint64_t hash = 0;
     void *dev = nullptr;         // device copy of the pointer array
     void *staging = nullptr;     // pinned host buffer the upload reads
-    void *done = nullptr;        // hipEvent_t recorded after the last launch that read `dev`
-    void *last_stream = nullptr; // stream of that launch
-    bool recorded = false;       // `done` has been recorded at least once
-    bool many_streams = false;   // read on more than one stream since the last upload
+    std::vector<SlotReader> readers;  // one entry per stream that has read the slot
+    bool untracked = false;      // a read could not be recorded: reuse waits for the device
     void *uploaded = nullptr;    // hipEvent_t recorded after the upload of the current set
     void *upload_stream = nullptr;
     bool upload_done = false;    // the upload is known to have finished
@@ -62,6 +67,7 @@ struct DeviceState {
 };
 
 constexpr size_t kPtrCacheEntries = 8;
+constexpr size_t kMaxSlotReaders = 16;   // streams tracked per pointer-table slot
 
 }  // namespace tide
 

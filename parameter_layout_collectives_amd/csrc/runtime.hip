@@ -82,7 +82,8 @@ void free_state(DeviceState *ds) {
         for (auto &pt : *cache) {
             (void)hipFree(pt.dev);
             (void)hipHostFree(pt.staging);
-            if (pt.done) (void)hipEventDestroy(static_cast<hipEvent_t>(pt.done));
+            for (const SlotReader &r : pt.readers)
+                (void)hipEventDestroy(static_cast<hipEvent_t>(r.event));
             if (pt.uploaded) (void)hipEventDestroy(static_cast<hipEvent_t>(pt.uploaded));
         }
     delete ds;
@@ -175,17 +176,46 @@ struct PtrKey {
 };
 
 // Records that work on `stream` reads the slot: called after its upload
-// and after every launch that reads it.
+// and after every launch that reads it.  Each stream gets its own event
+// (created on its first read of this slot), so reusing the slot later waits
+// for exactly the streams that read it.
 tide_status mark_read(PtrTable *pt, hipStream_t stream) {
-    if (pt->recorded && pt->last_stream != static_cast<void *>(stream)) pt->many_streams = true;
-    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pt->done), stream);
-    if (e != hipSuccess) {
-        // The event no longer covers every reader: reuse waits for the device.
-        pt->recorded = pt->many_streams = true;
-        return hip_fail("pointer table: hipEventRecord", e);
+    SlotReader *reader = nullptr;
+    for (SlotReader &r : pt->readers)
+        if (r.stream == static_cast<void *>(stream)) reader = &r;
+    hipError_t e = hipSuccess;
+    if (!reader && pt->readers.size() >= kMaxSlotReaders) {
+        // A new stream takes over the entry of a stream whose last read has
+        // finished (or, if none has, of the first one once it finishes).
+        for (SlotReader &r : pt->readers)
+            if (!reader && hipEventQuery(static_cast<hipEvent_t>(r.event)) == hipSuccess)
+                reader = &r;
+        if (!reader) {
+            reader = &pt->readers.front();
+            e = hipEventSynchronize(static_cast<hipEvent_t>(reader->event));
+        }
+        reader->stream = static_cast<void *>(stream);
     }
-    pt->recorded = true;
-    pt->last_stream = static_cast<void *>(stream);
+    if (!reader && e == hipSuccess) {
+        hipEvent_t ev = nullptr;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) {
+            try {
+                pt->readers.push_back({static_cast<void *>(stream), ev});
+                reader = &pt->readers.back();
+            } catch (const std::bad_alloc &) {
+                (void)hipEventDestroy(ev);
+                pt->untracked = true;
+                return fail(TIDE_E_NOMEM, "pointer table: out of host memory");
+            }
+        }
+    }
+    if (e == hipSuccess) e = hipEventRecord(static_cast<hipEvent_t>(reader->event), stream);
+    if (e != hipSuccess) {
+        // No event covers this read: reuse waits for the device.
+        pt->untracked = true;
+        return hip_fail("pointer table: recording its reader", e);
+    }
     return TIDE_OK;
 }
 
@@ -220,33 +250,39 @@ tide_status order_after_upload(PtrTable *pt, hipStream_t stream) {
     return TIDE_OK;
 }
 
-// Allocates a slot's device table, pinned staging buffer and events.
+// Allocates a slot's device table, pinned staging buffer and upload event
+// (reader events are created as streams read the slot).
 tide_status new_slot(size_t bytes, PtrTable *pt) {
     hipError_t e = hipMalloc(&pt->dev, bytes);
     if (e == hipSuccess) e = hipHostMalloc(&pt->staging, bytes, hipHostMallocDefault);
-    hipEvent_t ev = nullptr, up = nullptr;
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    hipEvent_t up = nullptr;
     if (e == hipSuccess) e = hipEventCreateWithFlags(&up, hipEventDisableTiming);
-    pt->done = ev;
     pt->uploaded = up;
     if (e == hipSuccess) return TIDE_OK;
     (void)hipFree(pt->dev);
     (void)hipHostFree(pt->staging);
-    if (ev) (void)hipEventDestroy(ev);
     if (up) (void)hipEventDestroy(up);
-    pt->dev = pt->staging = pt->done = pt->uploaded = nullptr;
+    pt->dev = pt->staging = pt->uploaded = nullptr;
     if (e == hipErrorOutOfMemory) return fail(TIDE_E_NOMEM, "pointer table: allocation");
     return hip_fail("pointer table: allocation", e);
 }
 
 // Waits until no launch can still read the slot's device table (and so no
-// upload can still read its staging buffer).  A slot read on one stream
-// waits for its event; one read on several streams waits for the device.
+// upload can still read its staging buffer): the latest event of every
+// stream that read it.  Only a read that could not be recorded makes it
+// wait for the whole device.
 tide_status drain_slot(PtrTable *pt) {
-    if (!pt->recorded) return TIDE_OK;
-    hipError_t e = pt->many_streams ? hipDeviceSynchronize()
-                                    : hipEventSynchronize(static_cast<hipEvent_t>(pt->done));
-    if (e != hipSuccess) return hip_fail("pointer table: waiting for its last reader", e);
+    hipError_t e = hipSuccess;
+    if (pt->untracked) {
+        e = hipDeviceSynchronize();
+        if (e == hipSuccess) pt->untracked = false;
+    } else {
+        for (const SlotReader &r : pt->readers) {
+            e = hipEventSynchronize(static_cast<hipEvent_t>(r.event));
+            if (e != hipSuccess) break;
+        }
+    }
+    if (e != hipSuccess) return hip_fail("pointer table: waiting for its last readers", e);
     return TIDE_OK;
 }
 
@@ -295,7 +331,6 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const P
         } catch (const std::bad_alloc &) {
             (void)hipFree(fresh.dev);
             (void)hipHostFree(fresh.staging);
-            (void)hipEventDestroy(static_cast<hipEvent_t>(fresh.done));
             (void)hipEventDestroy(static_cast<hipEvent_t>(fresh.uploaded));
             return fail(TIDE_E_NOMEM, "pointer table: out of host memory");
         }
@@ -310,10 +345,10 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const P
         tide_status drained = drain_slot(pt);
         if (drained != TIDE_OK) return drained;
     }
-    // The slot holds no valid set until the upload is enqueued.
+    // The slot holds no valid set until the upload is enqueued.  Its reader
+    // events stay: they are all complete now and are re-recorded on use.
     pt->hash = 0;
     pt->key.clear();
-    pt->recorded = pt->many_streams = false;
     try {
         pt->key.resize(key.size());
     } catch (const std::bad_alloc &) {
@@ -451,12 +486,30 @@ unsigned grid_size(const DeviceLimits &lim, int64_t ntiles, uint32_t flags, int3
     return static_cast<unsigned>(std::max<int64_t>(g, 1));
 }
 
+// Waits, before the plan's device tables are freed, for every launch that
+// may read them: the events of every stream that read one of the plan's
+// pointer-table slots on this device.  Launches captured into a graph
+// record no event; while a slot is held by a captured launch (or a read went
+// unrecorded) the whole device is waited for instead.
 void release_device_states(const tide_plan *p) {
     std::lock_guard<std::mutex> lock(p->mu);
     int cur = -1;
     const bool have_cur = hipGetDevice(&cur) == hipSuccess;
     for (DeviceState *ds : p->devs) {
-        if (hipSetDevice(ds->device) == hipSuccess) (void)hipDeviceSynchronize();
+        if (hipSetDevice(ds->device) == hipSuccess) {
+            bool whole_device = false;
+            for (auto *cache : {&ds->rs_cache, &ds->ag_cache, &ds->pack_cache, &ds->slots_cache})
+                for (const PtrTable &pt : *cache) whole_device |= pt.pinned || pt.untracked;
+            if (whole_device) {
+                (void)hipDeviceSynchronize();
+            } else {
+                for (auto *cache :
+                     {&ds->rs_cache, &ds->ag_cache, &ds->pack_cache, &ds->slots_cache})
+                    for (const PtrTable &pt : *cache)
+                        for (const SlotReader &r : pt.readers)
+                            (void)hipEventSynchronize(static_cast<hipEvent_t>(r.event));
+            }
+        }
         free_state(ds);
     }
     p->devs.clear();

@@ -641,3 +641,71 @@ def test_table_slots_under_concurrent_eviction(orc):
         for t in range(2):
             got = outs[t][j].cpu().numpy()
             assert same_f32(got, want), (t, j, first_mismatch(got, want))
+
+
+def _sleep_cycles_for(ms):
+    """torch.cuda._sleep cycle count for about `ms` milliseconds (measured)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    torch.cuda._sleep(5_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return int(5_000_000 * ms / max(a.elapsed_time(b), 1e-3))
+
+
+def test_slot_reuse_waits_only_for_its_readers(orc):
+    """Every cached pointer set is read on two streams; replacing one then
+    waits for those two streams' events only, not for a long (bounded) spin
+    on a third stream that never read it."""
+    import time
+    shapes = [(29, 7), (4100,)]
+    N = 3
+    plan = tide.Plan(shapes, N)
+    sets = [to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=4000 + 10 * j))
+            for j in range(9)]
+    a, b, c = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    scratch = fresh_out(plan.S)
+    for j in range(8):                       # 8 slots, each read on a and b
+        tide.rs(plan, 0, sets[j], scratch, stream=a)
+        tide.rs(plan, 0, sets[j], scratch, stream=b)
+    torch.cuda.synchronize()
+    spin = _sleep_cycles_for(800.0)
+    out = fresh_out(plan.S)
+    note("slot reuse beside an 800 ms spin on an unrelated stream")
+    with torch.cuda.stream(c):
+        torch.cuda._sleep(spin)
+    t0 = time.perf_counter()
+    tide.rs(plan, 2, sets[8], out, stream=a)  # replaces the slot of set 0
+    host_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    assert host_s < 0.4, f"replacing a slot waited {host_s:.3f} s (the unrelated spin)"
+    want = expected_rs(orc, shapes, N, 2, sets[8], plan)
+    got = out.cpu().numpy()
+    assert same_f32(got, want), first_mismatch(got, want)
+
+
+def test_one_set_read_on_many_streams(orc):
+    """20 streams read one cached set (more than the 16 tracked per slot),
+    then 9 other sets replace every slot: every result equals the oracle."""
+    shapes = [(31, 6), (2049,)]
+    N = 4
+    plan = tide.Plan(shapes, N)
+    base = to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=5000))
+    others = [to_dev(workloads.random_grads_for_shapes(shapes, N, seed_base=5100 + 10 * j))
+              for j in range(9)]
+    streams = [torch.cuda.Stream() for _ in range(20)]
+    outs = [fresh_out(plan.S) for _ in streams]
+    note("one pointer set on 20 streams, then 9 evicting sets")
+    for k, (s, o) in enumerate(zip(streams, outs)):
+        tide.rs(plan, k % N, base, o, stream=s)
+    outs2 = [fresh_out(plan.S) for _ in others]
+    for j, (g, o) in enumerate(zip(others, outs2)):
+        tide.rs(plan, j % N, g, o, stream=streams[j])
+    torch.cuda.synchronize()
+    for k, o in enumerate(outs):
+        want = expected_rs(orc, shapes, N, k % N, base, plan)
+        assert same_f32(o.cpu().numpy(), want), k
+    for j, o in enumerate(outs2):
+        want = expected_rs(orc, shapes, N, j % N, others[j], plan)
+        assert same_f32(o.cpu().numpy(), want), j
