@@ -23,7 +23,7 @@ namespace tide {
 #define TIDE_AG_TILE_SMALL 32768
 #endif
 #ifndef TIDE_RS_TILE_SMALL
-#define TIDE_RS_TILE_SMALL 2048
+#define TIDE_RS_TILE_SMALL 1024
 #endif
 
 // Elements of one parameter segment handled by one reduce-scatter tile, and
@@ -73,7 +73,7 @@ struct Tile {
 #define TIDE_RS_RB 8
 #endif
 #ifndef TIDE_SMALL_CPL
-#define TIDE_SMALL_CPL 2
+#define TIDE_SMALL_CPL 1
 #endif
 #ifndef TIDE_SMALL_RB
 #define TIDE_SMALL_RB 16

@@ -42,10 +42,11 @@ namespace {
 // Small-footprint TIDE-RS for at most this many ranks runs the default
 // kernel shape (4 chunks per lane over 4096-element tiles) under the
 // small-footprint LDS reservation; for more ranks, the lighter small shape
-// (2 chunks per lane, 2048-element tiles, 16-rank batches), whose shorter
+// (1 chunk per lane, 1024-element tiles, 16-rank batches), whose shorter
 // workgroups hand CUs back sooner.  Beside a bf16 8192^3 GEMM the default
-// shape cost the GEMM 0.3% (8 ranks) and 3.5% (16 ranks), but 9.9% at 64
-// ranks against the small shape's 4.6-7.1%.
+// shape cost the GEMM 0.3% (8 ranks) and 3.5% (16 ranks) but 9.9% at 64
+// ranks; at 64 ranks 2048-element tiles with 2 chunks per lane cost it
+// 8.9-11.2% and the shipped 1024-element shape 6.8%.
 #ifndef TIDE_SMALL_FEW_RANKS
 #define TIDE_SMALL_FEW_RANKS 16
 #endif
