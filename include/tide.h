@@ -132,7 +132,9 @@ typedef struct tide_plan tide_plan;
 /* Flag, tide_rs only: write the mean instead of the sum - each rank-order
  * fp32 sum divided by N with one correctly rounded binary32 division
  * (apxml "Communication volume analysis" §"分片中的通信原语" describes the
- * gradient reduce-scatter as averaging).  Padding and gaps stay +0.0f. */
+ * gradient reduce-scatter as averaging).  Padding and gaps stay +0.0f.  When
+ * N is a power of two the kernel multiplies by 1/N instead, which rounds the
+ * same exact value once and so gives the same bits. */
 #define TIDE_F_AVG 0x4u
 
 /* ---------------------------------------------------------------------- */

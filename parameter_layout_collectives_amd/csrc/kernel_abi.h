@@ -114,6 +114,18 @@ enum GradType { kBf16 = 0, kF16 = 1, kF32 = 2 };
 // result rounded once to bf16 (nearest, ties to even).
 enum OutType { kOutF32 = 0, kOutBf16 = 1 };
 
+// How a TIDE-RS launch turns the rank-order sum into the mean (TIDE_F_AVG):
+// not at all, by one correctly rounded division by N, or, when N is a power
+// of two, by one multiplication by 1/N = 2^-k.  The exact quotient x/2^k and
+// the exact product x*2^-k are the same real number, and each operation
+// rounds it once, so the two give identical bits (subnormal results, zeros,
+// infinities included; a NaN stays a NaN).
+enum AvgMode { kAvgNone = 0, kAvgDiv = 1, kAvgMul = 2 };
+inline int avg_mode(int N, bool avg) {
+    if (!avg) return kAvgNone;
+    return (N & (N - 1)) == 0 ? kAvgMul : kAvgDiv;
+}
+
 // Everything one TIDE-RS launch needs.  ptrs is the param-major pointer
 // table (entry i*N + r = rank r's gradient of parameter i) plus kPtrPad
 // null entries.  vec_in: every gradient pointer is 16-byte aligned; vec_out:
@@ -124,7 +136,7 @@ struct RsLaunch {
     const Tile *tiles;
     int64_t ntiles;
     const char *const *ptrs;
-    int N, R, avg;
+    int N, R, avg;               // avg: an AvgMode
     void *out;                   // S elements of the output type
     int vec_in, vec_out;
     unsigned grid;

@@ -160,7 +160,10 @@ __device__ __forceinline__ void rs_elems(const char *const *__restrict__ P, int 
         const int64_t byte = (src + k) * G::ES;
         float acc = G::one(gload_ptr<char>(P[0] + byte));
         for (int r = 1; r < N; r++) acc = acc + G::one(gload_ptr<char>(P[r] + byte));
-        if (avg) acc = acc / static_cast<float>(N);
+        if (avg == kAvgMul)
+            acc = acc * (1.0f / static_cast<float>(N));
+        else if (avg == kAvgDiv)
+            acc = acc / static_cast<float>(N);
         Out<OT>::one(o + k * Out<OT>::ES, acc);
     }
 }
@@ -227,7 +230,9 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t v, int64_t ntiles) {
 // Tile t covers elements [k0, k0 + TILE) of parameter i's span in the rank
 // block (its segment plus any alignment gap after it).  For rank R:
 //   k <  L(R,i):  out[off_i + k] = sum_{r=0..N-1} widen(G[r][i][R*seg_i + k])
-//                 (divided by N when avg is set)
+//                 (divided by N when avg is set: kAvgDiv divides, kAvgMul
+//                 multiplies by 1/N, which the host picks only when N is a
+//                 power of two, where both give the same bits)
 //   k >= L(R,i):  out[off_i + k] = +0.0f   (padding rows, alignment gap)
 // ptrs is param-major: ptrs[i*N + r] = G[r][i].  OT: fp32 output, or the
 // fp32 result rounded to bf16 (padding then +0 in bf16).
@@ -294,7 +299,13 @@ __global__ __launch_bounds__(BLOCK) void rs_kernel(const ParamDesc *__restrict__
                 rs_batch<IT, CPL, RB, true>(P, 0, min(N, RB), first_byte, in_off, acc);
                 for (int r0 = RB; r0 < N; r0 += RB)
                     rs_batch<IT, CPL, RB, false>(P, r0, min(N - r0, RB), first_byte, in_off, acc);
-                if (avg) {
+                if (avg == kAvgMul) {
+                    const float inv = 1.0f / static_cast<float>(N);   // exact: N = 2^k
+#pragma unroll
+                    for (int j = 0; j < CPL; j++)
+                        acc[j] = f32x4{acc[j].x * inv, acc[j].y * inv, acc[j].z * inv,
+                                       acc[j].w * inv};
+                } else if (avg == kAvgDiv) {
                     const float n = static_cast<float>(N);
 #pragma unroll
                     for (int j = 0; j < CPL; j++)

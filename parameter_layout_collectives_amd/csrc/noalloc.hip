@@ -185,7 +185,7 @@ extern "C" tide_status tide_rs_noalloc(const tide_plan *plan, int32_t rank,
                                 reinterpret_cast<const char *const *>(dev->ptr + L.ptrs),
                                 N,
                                 rank,
-                                (flags & TIDE_F_AVG) ? 1 : 0,
+                                tide::avg_mode(plan->N, (flags & TIDE_F_AVG) != 0),
                                 out,
                                 aligned16 ? 1 : 0,
                                 (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,

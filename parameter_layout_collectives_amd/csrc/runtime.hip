@@ -558,7 +558,7 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
                            static_cast<const char *const *>(pt->dev),
                            plan->N,
                            rank,
-                           (flags & TIDE_F_AVG) ? 1 : 0,
+                           tide::avg_mode(plan->N, (flags & TIDE_F_AVG) != 0),
                            out,
                            pt->aligned16 ? 1 : 0,
                            (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,
@@ -769,7 +769,7 @@ extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
                            static_cast<const char *const *>(pt->dev),
                            N,
                            rank,
-                           (flags & TIDE_F_AVG) ? 1 : 0,
+                           tide::avg_mode(plan->N, (flags & TIDE_F_AVG) != 0),
                            out,
                            pt->aligned16 ? 1 : 0,
                            (reinterpret_cast<uintptr_t>(out) & 15) == 0 ? 1 : 0,

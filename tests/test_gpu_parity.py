@@ -281,6 +281,29 @@ def test_f16_special_values(orc):
             check_rs_typed(orc, [(n // 4, 4)], N, grads, R, "f16", avg)
 
 
+@pytest.mark.parametrize("N", [2, 6, 8, 16])
+def test_f32_mean_subnormal_and_special_results(orc, N):
+    """The mean of fp32 gradients whose sums are subnormal, tiny normal,
+    huge (overflowing to infinity), signed zeros, infinities and NaNs.  At
+    power-of-two N the kernel multiplies by 1/N, otherwise it divides; the
+    oracle always divides, and the bits must agree either way."""
+    n = 4096 + 36
+    pool = np.array([0x00000001, 0x80000001, 0x00000003, 0x007FFFFF, 0x807FFFFF, 0x00800000,
+                     0x00800001, 0x80800000, 0x01000000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F000000,
+                     0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0x3F800000,
+                     0x00400000, 0x00000010], np.uint32)
+    rng = np.random.default_rng(17 + N)
+    grads = []
+    for r in range(N):
+        bits = pool[rng.integers(0, len(pool), size=n)]
+        bits[:256] = pool[rng.integers(0, 7, size=256)]     # subnormal sums
+        grads.append([torch.from_numpy(bits.view(np.int32)).view(torch.float32).to(DEV)
+                      .reshape(n // 4, 4)])
+    for R in sorted({0, N - 1}):
+        check_rs_typed(orc, [(n // 4, 4)], N, grads, R, "f32", True)
+        check_rs_typed(orc, [(n // 4, 4)], N, grads, R, "f32", True, small=True)
+
+
 # ---------------------------------------------------------------------------
 # reduce-scatter with a bf16 shard (the fp32 result rounded once)
 # ---------------------------------------------------------------------------
