@@ -39,6 +39,8 @@ Reported (one JSON line on stdout, progress on stderr):
   copy ceilings           torch's device copy and the library's own copy;
   cpu_baseline the CPU oracle on the same step's inputs (host cores), and
               the tiny workload's step on one thread.
+The printed line leaves out the per-repeat lists of the co-run experiments
+(their medians stay); --detail FILE writes the full result as well.
 
 Algorithmic bytes (what the method must move; the fp32 pack buffer and the
 copy-out pass it avoids are not counted):
@@ -1171,6 +1173,16 @@ def corun_summary(results):
     return rows
 
 
+def compact(obj):
+    """The bench line without the per-repeat lists of the co-run experiments
+    (their medians stay); --detail FILE keeps everything."""
+    if isinstance(obj, dict):
+        return {k: compact(v) for k, v in obj.items() if k not in ("progress_runs", "runs")}
+    if isinstance(obj, list):
+        return [compact(v) for v in obj]
+    return obj
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1194,6 +1206,9 @@ def main():
                     help="skip the tide_rs flag variants (bf16 shard, mean), the small-footprint "
                          "alone timing, the tiny workload, the two-stage reduce-scatter and the "
                          "layout-conversion leg")
+    ap.add_argument("--detail", default="",
+                    help="also write the full result, per-repeat co-run figures included, to "
+                         "this JSON file")
     ap.add_argument("--corun-grids", default="128",
                     help="comma-separated persistent grid sizes (max_workgroups) for extra "
                          "small-footprint co-run modes, or 'none'")
@@ -1365,7 +1380,10 @@ def main():
     }
     if args.lib:
         line["library"] = args.lib
-    print(json.dumps(line), flush=True)
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump(line, f)
+    print(json.dumps(compact(line)), flush=True)
 
 
 if __name__ == "__main__":

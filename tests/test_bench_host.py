@@ -88,3 +88,13 @@ def test_unknown_leg_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "unknown" in r.stderr
+
+
+def test_compact_line_drops_per_repeat_lists_only():
+    line = {"value": 1.0, "corun": {"default": {"exposed_ms": 2.0, "progress_runs": [{"a": 1}],
+                                                "makespan": {"serial_ms": 3.0, "runs": [{}]}}},
+            "corun_summary": [{"mode": "default", "exposed_ms": 2.0}]}
+    got = bench.compact(line)
+    assert got == {"value": 1.0, "corun": {"default": {"exposed_ms": 2.0,
+                                                       "makespan": {"serial_ms": 3.0}}},
+                   "corun_summary": [{"mode": "default", "exposed_ms": 2.0}]}
