@@ -118,7 +118,7 @@ void release_device_states(const tide_plan *p);
 tide_status query_limits(int device, DeviceLimits *out);   // device attributes (no allocation)
 // Kernel shape, tile size and LDS reservation of a reduce-scatter launch.
 struct RsPolicy {
-    bool small_kernel;   // the small-footprint kernel shape over kRsTileSmall tiles
+    RsKernelShape shape; // kRsSmall walks the kRsTileSmall tile list, the others kRsTile
     int64_t tile;        // kRsTile or kRsTileSmall
     int lds;
 };

@@ -72,6 +72,17 @@ struct Tile {
 #ifndef TIDE_RS_RB
 #define TIDE_RS_RB 8
 #endif
+// Default TIDE-RS launches for at least TIDE_RS_WIDE_N ranks load the ranks
+// in batches of TIDE_RS_WIDE_RB instead of TIDE_RS_RB.  With the N gradients
+// of one element at the same offset in N buffers, fewer of them in flight at
+// once per wave measured faster from 16 ranks up (the MoE layer at 16 ranks
+// +3.2%, the 70B shapes at 24 ranks +3%) and slower at 8 and 12.
+#ifndef TIDE_RS_WIDE_N
+#define TIDE_RS_WIDE_N 16
+#endif
+#ifndef TIDE_RS_WIDE_RB
+#define TIDE_RS_WIDE_RB 2
+#endif
 #ifndef TIDE_SMALL_CPL
 #define TIDE_SMALL_CPL 1
 #endif
@@ -103,8 +114,14 @@ constexpr int kAgVecsPerLane = TIDE_AG_U;
 // Spare (null) entries after the reduce-scatter pointer table: a batch of RB
 // ranks loads its RB pointers unconditionally.
 constexpr size_t kPtrPad = 32;
-static_assert(TIDE_RS_RB <= static_cast<int>(kPtrPad) && TIDE_SMALL_RB <= static_cast<int>(kPtrPad),
+static_assert(TIDE_RS_RB <= static_cast<int>(kPtrPad) && TIDE_SMALL_RB <= static_cast<int>(kPtrPad) &&
+                  TIDE_RS_WIDE_RB <= static_cast<int>(kPtrPad),
               "rank batch larger than the pointer-table padding");
+
+// The TIDE-RS kernel shapes: the default one (4096-element tiles, 8-rank
+// batches), the same over 2-rank batches for many ranks, and the
+// small-footprint one (its own tile list).
+enum RsKernelShape { kRsDefault = 0, kRsWide = 1, kRsSmall = 2 };
 
 // Gradient element types.  Each widens exactly to fp32: bf16 is the top
 // half of an fp32 pattern, every fp16 value is an fp32 value, fp32 is kept.
@@ -172,10 +189,12 @@ struct PackLaunch {
     hipStream_t stream;
 };
 
-// Enqueue one launch.  `small` selects the small-footprint tile list's
-// kernel shape (the caller passes that tile list).  Returns the HIP error of
+// Enqueue one launch.  For TIDE-RS `shape` picks the kernel shape; for the
+// other two `small` selects the small-footprint kernel shape.  The caller
+// passes the matching tile list (kRsSmall and `small` walk the
+// small-footprint tile lists).  Returns the HIP error of
 // the launch (or of allowing its LDS reservation).
-hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, bool small);
+hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, RsKernelShape shape);
 hipError_t launch_ag(const AgLaunch &a, bool small);
 hipError_t launch_pack(const PackLaunch &a, bool small);
 

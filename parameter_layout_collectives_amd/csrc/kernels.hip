@@ -486,19 +486,24 @@ hipError_t allow_lds(const void *kernel, int bytes) {
     return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-// Default launches: one 256-lane workgroup per 4096-element tile.  Small-
-// footprint launches: the small tile list and its kernel shape.
-template <int IT, int OT, bool SMALL>
+// Default launches: one 256-lane workgroup per 4096-element tile (8-rank
+// batches, or 2-rank batches for many ranks).  Small-footprint launches:
+// the small tile list and its kernel shape.
+template <int IT, int OT, int SHAPE>
 hipError_t launch_rs_t(const RsLaunch &a) {
-    auto k = SMALL ? rs_kernel<IT, OT, TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_RB,
-                               TIDE_SMALL_PACE, TIDE_XMAP_RS, kRsTileSmall>
-                   : rs_kernel<IT, OT, kBlock, kRsChunksPerLane, TIDE_RS_RB, 0, TIDE_XMAP_RS,
-                               kRsTile>;
+    auto k = SHAPE == kRsSmall
+                 ? rs_kernel<IT, OT, TIDE_SMALL_BLOCK, TIDE_SMALL_CPL, TIDE_SMALL_RB,
+                             TIDE_SMALL_PACE, TIDE_XMAP_RS, kRsTileSmall>
+             : SHAPE == kRsWide
+                 ? rs_kernel<IT, OT, kBlock, kRsChunksPerLane, TIDE_RS_WIDE_RB, 0, TIDE_XMAP_RS,
+                             kRsTile>
+                 : rs_kernel<IT, OT, kBlock, kRsChunksPerLane, TIDE_RS_RB, 0, TIDE_XMAP_RS,
+                             kRsTile>;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(k), a.lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SMALL ? TIDE_SMALL_BLOCK : kBlock), a.lds, a.stream,
-                       a.pd, a.tiles, a.ntiles, a.ptrs, a.N, a.R, a.avg, a.out, a.vec_in,
-                       a.vec_out);
+    hipLaunchKernelGGL(k, dim3(a.grid), dim3(SHAPE == kRsSmall ? TIDE_SMALL_BLOCK : kBlock),
+                       a.lds, a.stream, a.pd, a.tiles, a.ntiles, a.ptrs, a.N, a.R, a.avg, a.out,
+                       a.vec_in, a.vec_out);
     return hipGetLastError();
 }
 
@@ -525,21 +530,30 @@ hipError_t launch_pack_t(const PackLaunch &a) {
     return hipGetLastError();
 }
 
+template <int IT, int OT>
+hipError_t launch_rs_s(const RsLaunch &a, RsKernelShape shape) {
+    switch (shape) {
+    case kRsSmall: return launch_rs_t<IT, OT, kRsSmall>(a);
+    case kRsWide: return launch_rs_t<IT, OT, kRsWide>(a);
+    default: return launch_rs_t<IT, OT, kRsDefault>(a);
+    }
+}
+
 template <int OT>
-hipError_t launch_rs_o(const RsLaunch &a, GradType type, bool small) {
+hipError_t launch_rs_o(const RsLaunch &a, GradType type, RsKernelShape shape) {
     switch (type) {
-    case kF32: return small ? launch_rs_t<kF32, OT, true>(a) : launch_rs_t<kF32, OT, false>(a);
-    case kF16: return small ? launch_rs_t<kF16, OT, true>(a) : launch_rs_t<kF16, OT, false>(a);
-    default: return small ? launch_rs_t<kBf16, OT, true>(a) : launch_rs_t<kBf16, OT, false>(a);
+    case kF32: return launch_rs_s<kF32, OT>(a, shape);
+    case kF16: return launch_rs_s<kF16, OT>(a, shape);
+    default: return launch_rs_s<kBf16, OT>(a, shape);
     }
 }
 
 }  // namespace
 
-hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, bool small) {
+hipError_t launch_rs(const RsLaunch &a, GradType type, OutType out, RsKernelShape shape) {
     (void)hipGetLastError();
-    return out == kOutBf16 ? launch_rs_o<kOutBf16>(a, type, small)
-                           : launch_rs_o<kOutF32>(a, type, small);
+    return out == kOutBf16 ? launch_rs_o<kOutBf16>(a, type, shape)
+                           : launch_rs_o<kOutF32>(a, type, shape);
 }
 
 hipError_t launch_ag(const AgLaunch &a, bool small) {

@@ -196,7 +196,7 @@ extern "C" tide_status tide_rs_noalloc(const tide_plan *plan, int32_t rank,
                                 : (flags & TIDE_F_GRAD_F16) ? tide::kF16
                                                             : tide::kBf16;
     const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
-    e = tide::launch_rs(launch, type, otype, pol.small_kernel);
+    e = tide::launch_rs(launch, type, otype, pol.shape);
     if (e != hipSuccess) return tide::hip_fail("tide_rs_noalloc: kernel launch", e);
     tide::clear_error();
     return TIDE_OK;

@@ -389,7 +389,7 @@ tide_status pointer_table(DeviceState *ds, std::vector<PtrTable> &cache, const P
 
 // The reduce-scatter launch for `flags`: kernel shape, tile list, LDS.
 struct RsShape {
-    bool small_kernel;   // the small-footprint kernel shape and its tile list
+    RsKernelShape shape; // kernel shape (kRsSmall: the small-footprint tile list)
     const Tile *tiles;
     int64_t ntiles;
     int lds;
@@ -398,10 +398,11 @@ struct RsShape {
 RsShape rs_shape(const tide_plan *p, const DeviceState *ds, uint32_t flags) {
     const RsPolicy pol = rs_policy(ds->lim, p->N, flags);
     RsShape r;
-    r.small_kernel = pol.small_kernel;
-    r.tiles = static_cast<const Tile *>(pol.small_kernel ? ds->d_rs_tiles_small : ds->d_rs_tiles);
-    r.ntiles = static_cast<int64_t>(pol.small_kernel ? p->rs_tiles_small.size()
-                                                     : p->rs_tiles.size());
+    const bool small_tiles = pol.shape == kRsSmall;
+    r.shape = pol.shape;
+    r.tiles = static_cast<const Tile *>(small_tiles ? ds->d_rs_tiles_small : ds->d_rs_tiles);
+    r.ntiles = static_cast<int64_t>(small_tiles ? p->rs_tiles_small.size()
+                                                : p->rs_tiles.size());
     r.lds = pol.lds;
     return r;
 }
@@ -457,8 +458,9 @@ tide_status query_limits(int dev, DeviceLimits *out) {
 RsPolicy rs_policy(const DeviceLimits &lim, int32_t N, uint32_t flags) {
     const bool small = (flags & TIDE_F_SMALL_FOOTPRINT) != 0;
     RsPolicy r;
-    r.small_kernel = small && N > TIDE_SMALL_FEW_RANKS;
-    r.tile = r.small_kernel ? kRsTileSmall : kRsTile;
+    r.shape = small ? (N > TIDE_SMALL_FEW_RANKS ? kRsSmall : kRsDefault)
+                    : (N >= TIDE_RS_WIDE_N ? kRsWide : kRsDefault);
+    r.tile = r.shape == kRsSmall ? kRsTileSmall : kRsTile;
     r.lds = small ? lim.small_lds : lim.rs_cap_lds;
     return r;
 }
@@ -569,7 +571,7 @@ extern "C" tide_status tide_rs(const tide_plan *plan, int32_t rank, const void *
                                 : (flags & TIDE_F_GRAD_F16) ? tide::kF16
                                                             : tide::kBf16;
     const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
-    hipError_t e = tide::launch_rs(L, type, otype, shape.small_kernel);
+    hipError_t e = tide::launch_rs(L, type, otype, shape.shape);
     if (e != hipSuccess) return tide::hip_fail("tide_rs: kernel launch", e);
     st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;
@@ -780,7 +782,7 @@ extern "C" tide_status tide_rs_slots(const tide_plan *plan, int32_t rank,
                                 : (flags & TIDE_F_GRAD_F16) ? tide::kF16
                                                             : tide::kBf16;
     const tide::OutType otype = (flags & TIDE_F_OUT_BF16) ? tide::kOutBf16 : tide::kOutF32;
-    hipError_t e = tide::launch_rs(L, type, otype, shape.small_kernel);
+    hipError_t e = tide::launch_rs(L, type, otype, shape.shape);
     if (e != hipSuccess) return tide::hip_fail("tide_rs_slots: kernel launch", e);
     st = tide::after_launch(pt, static_cast<hipStream_t>(stream), capturing);
     if (st != TIDE_OK) return st;

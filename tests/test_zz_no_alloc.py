@@ -51,6 +51,7 @@ CASES = [
      [3], {"small": True, "avg": True, "out_bf16": True}),
     ("ragged 40 params, 24 ranks, small footprint", _ragged_shapes(40, 9), 24, [0, 23],
      {"small": True}),
+    ("ragged 40 params, 20 ranks (2-rank batches)", _ragged_shapes(40, 11), 20, [0, 19], {}),
     ("tiny, 4 ranks", workloads.WORKLOADS["tiny"].shapes, 4, [0, 1, 2, 3], {}),
 ]
 
