@@ -606,6 +606,14 @@ def layout_conversion_leg(step, tokens=8192, reps=3):
     return res
 
 
+def fit_fixed_cost(p1, p2):
+    """t = t0 + B / r through two (bytes, microseconds) points: (t0 in us,
+    r in GB/s)."""
+    (b1, t1), (b2, t2) = p1, p2
+    r = (b2 - b1) / (t2 - t1) / 1e3
+    return t1 - b1 / (r * 1e3), r
+
+
 def fit_leg(w, repeats=(1, 4), reps=20, warmup=3):
     """Per-launch fixed cost and in-kernel rate of tide_rs and tide_ag on the
     workload's shapes: each call is timed on a bucket of K copies of the
@@ -645,9 +653,8 @@ def fit_leg(w, repeats=(1, 4), reps=20, warmup=3):
         gc.collect()
         torch.cuda.empty_cache()
     for name, p in pts.items():
-        (b1, t1), (b2, t2) = p[0], p[-1]
-        r = (b2 - b1) / (t2 - t1) / 1e3          # GB/s
-        t0 = t1 - b1 / (r * 1e3)
+        (b1, t1) = p[0]
+        t0, r = fit_fixed_cost(p[0], p[-1])
         res[name] = {"points_bytes_us": p, "fixed_us": t0, "in_kernel_GBps": r,
                      "in_kernel_pct_of_peak": 100.0 * r / HBM_PEAK_GBPS,
                      "single_GBps": b1 / t1 / 1e3}

@@ -98,3 +98,9 @@ def test_compact_line_drops_per_repeat_lists_only():
     assert got == {"value": 1.0, "corun": {"default": {"exposed_ms": 2.0,
                                                        "makespan": {"serial_ms": 3.0}}},
                    "corun_summary": [{"mode": "default", "exposed_ms": 2.0}]}
+
+
+def test_fixed_cost_fit():
+    # 10 us fixed plus 1 GB per 160 us (6.25 TB/s): two calls of 1 and 4 GB
+    t0, r = bench.fit_fixed_cost((1e9, 170.0), (4e9, 650.0))
+    assert abs(t0 - 10.0) < 1e-9 and abs(r - 6250.0) < 1e-6
