@@ -827,7 +827,7 @@ def collective_alone(partner, launch, nbytes, reps=8):
     return statistics.median(s.elapsed_time(e) for s, e in ev)
 
 
-def corun_progress(partner, launch, nbytes, t_alone, repeats=2):
+def corun_progress(partner, launch, nbytes, t_alone, repeats=3):
     """The progress experiment (see above); one dict per repeat."""
     sb, cur = partner.side, torch.cuda.current_stream()
     runs = []
@@ -879,7 +879,7 @@ def corun_progress(partner, launch, nbytes, t_alone, repeats=2):
     return runs
 
 
-def corun_makespan(partner, launch, nbytes, n, repeats=2):
+def corun_makespan(partner, launch, nbytes, n, repeats=3):
     """The makespan experiment (see above) with `n` collective calls: partner
     chain alone, collective chain alone, both together behind one gate;
     medians over `repeats`."""
@@ -987,12 +987,12 @@ CORUN_METHOD = (
     "progress: the partner's units run while a longer chain of collective calls (an event pair "
     "per call) runs on the other stream; during_partner_GBps = bytes completed inside the "
     "partner's window (calls pro-rated by their share inside) / that window; slowdown = median "
-    "unit time inside the chain / median unit time alone - 1 (median of 2 runs). makespan: a "
+    "unit time inside the chain / median unit time alone - 1 (median of 3 runs). makespan: a "
     "fixed partner chain and a fixed number of collective calls, the same for every launch mode "
     "(beside a GEMM: calls whose default-launch time alone is half the GEMM chain's; beside the "
     "layer step: one call per forward+backward), start together behind one gate; exposed = "
     "makespan - partner chain alone, serial = sum of the two alone, saving = serial - makespan "
-    "(median of 2 runs)")
+    "(median of 3 runs)")
 
 
 def _with_keys(partner_kind, leg):
