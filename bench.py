@@ -95,6 +95,14 @@ def rs_bytes(plan, R):
     return 2 * plan.world * real + 4 * plan.S
 
 
+def rs_bytes_mean(plan):
+    """Mean of rs_bytes over the ranks: the bytes per call of a chain whose
+    rank R rotates through 0..N-1 (equal to every rank's when every dim 0
+    divides by N; below it when the last ranks hold padding rows)."""
+    total = sum(rs_bytes(plan, r) for r in range(plan.world))
+    return total // plan.world if total % plan.world == 0 else total / plan.world
+
+
 def ag_bytes(plan):
     psi = sum(plan.real(r, i)[1] for r in range(plan.world) for i in range(plan.P))
     return 2 * psi + 2 * psi
@@ -156,7 +164,7 @@ class Step:
         self.gathered = workloads.random_bf16(N * S, seed=4242, sigma=w.sigma, device="cuda")
         self.params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in w.shapes]
         self.agt = tide.ag_tables(self.plan, self.gathered, self.params)
-        self.b_rs = rs_bytes(self.plan, 0)
+        self.b_rs = rs_bytes_mean(self.plan)
         self.b_ag = ag_bytes(self.plan)
         torch.cuda.synchronize()
 
@@ -634,7 +642,8 @@ def fit_leg(w, repeats=(1, 4), reps=20, warmup=3):
         params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in wk.shapes]
         agt = tide.ag_tables(plan, gathered, params)
         for name, fn, nbytes in (
-                ("tide_rs", lambda k: tide.rs(plan, k % N, table, out[k % N]), rs_bytes(plan, 0)),
+                ("tide_rs", lambda k: tide.rs(plan, k % N, table, out[k % N]),
+                 rs_bytes_mean(plan)),
                 ("tide_ag", lambda k: tide.ag(plan, None, None, tables=agt), ag_bytes(plan))):
             for k in range(warmup):
                 fn(k)
@@ -1030,7 +1039,7 @@ def corun_rs(partner, kind, w=None, step=None, grids=()):
         plan = tide.Plan(w.shapes, N)
         table = tide.grad_table(plan, grads)
         out = torch.empty(N, plan.S, dtype=torch.float32, device="cuda")
-        b_rs = rs_bytes(plan, 0)
+        b_rs = rs_bytes_mean(plan)
     res = dict(partner.describe(), workload=name, world=N, bytes_per_call=b_rs,
                method=CORUN_METHOD)
     n_calls = None

@@ -26,6 +26,7 @@ def test_algorithmic_bytes_70b_layer():
     assert psi == 855_654_400
     assert plan.S * w.world == psi
     assert bench.rs_bytes(plan, 0) == 2 * psi + 4 * plan.S == 2_139_136_000
+    assert bench.rs_bytes_mean(plan) == 2_139_136_000
     assert bench.ag_bytes(plan) == 4 * psi == 3_422_617_600
 
 
@@ -35,6 +36,8 @@ def test_rs_bytes_count_only_real_rows():
     assert plan.S == 14
     assert [bench.rs_bytes(plan, r) for r in range(4)] == \
         [2 * 4 * 14 + 4 * 14, 2 * 4 * 14 + 4 * 14, 2 * 4 * 7 + 4 * 14, 4 * 14]
+    # a chain with R rotating moves the mean: 2*4*(14+14+7+0)/4 + 4*14
+    assert bench.rs_bytes_mean(plan) == 2 * 4 * 35 / 4 + 4 * 14
 
 
 def test_counter_traffic_matches_its_run_only():
