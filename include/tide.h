@@ -287,7 +287,7 @@ tide_status tide_rs_slots(const tide_plan *plan, int32_t rank, const void *const
  * and then the reduce-scatter kernel.
  *   Limit: 32*P + 8*(P+1) + 8*(N*P + 32) bytes of tables, rounded up to 256,
  *   plus 16 bytes per tile (ceil(span_i / 4096) tiles per parameter, or
- *   ceil(span_i / 2048) with TIDE_F_SMALL_FOOTPRINT above 16 ranks) must fit
+ *   ceil(span_i / 1024) with TIDE_F_SMALL_FOOTPRINT above 16 ranks) must fit
  *   in 8 MiB; a larger plan returns TIDE_E_INVALID before anything is
  *   enqueued.
  *   Sharing: every call on one device uses that device's one array.  Calls

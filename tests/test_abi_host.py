@@ -421,3 +421,19 @@ def test_rs_noalloc_rejects_tables_beyond_its_scratch():
     ptrs = _ptrs([A + 16 * k for k in range(N * P)])
     assert _rs_noalloc(plan, 0, ptrs, A + (1 << 36)) == E_INVALID
     assert b"scratch" in L.tide_last_error()
+
+
+def test_rs_noalloc_limit_counts_small_footprint_tiles():
+    # Above 16 ranks the small footprint walks 1024-element tiles.  One
+    # [17, 2^29 + 64] parameter over 17 ranks: 2^17 + 1 default tiles (2 MiB
+    # of tile list) but 2^19 + 1 small-footprint tiles (8 MiB + 16 B), so only
+    # the small-footprint call exceeds the scratch array, by its exact need:
+    # 512 bytes of tables (440 rounded up to 256) plus 16 bytes per tile.
+    L = lib()
+    N = 17
+    plan = tide.Plan([(N, (1 << 29) + 64)], N)
+    assert plan.S == (1 << 29) + 64
+    ptrs = _ptrs([A + r * (1 << 35) for r in range(N)])
+    assert _rs_noalloc(plan, 0, ptrs, A + (1 << 40), flags=0x1) == E_INVALID
+    need = 512 + 16 * ((1 << 19) + 1)
+    assert f"need {need} bytes".encode() in L.tide_last_error()
