@@ -7,7 +7,10 @@ stream without a synchronisation in between: a larger plan first (many
 parameters, so its tables take several table-writing launches), then a
 smaller one, whose tables overwrite the first's while the first call's
 results are still to be checked.  The first call's output is also checked
-against the CPU oracle for one rank.
+against the CPU oracle for one rank.  Under HIP graph capture, where tide_rs
+refuses a pointer set its plan has not uploaded, tide_rs_noalloc captures
+such a set (its tables travel as kernel arguments) and every replay equals
+the oracle.
 """
 import numpy as np
 import pytest
@@ -15,7 +18,7 @@ import torch
 
 import parameter_layout_collectives_amd as tide
 import workloads
-from gpu_helpers import F32_SENTINEL, bits16, bits32, expected_rs, note
+from gpu_helpers import F32_SENTINEL, bits16, bits32, expected_rs, note, same_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +111,65 @@ def test_noalloc_repeated_calls_smaller_second():
         torch.cuda.synchronize()
         assert _same(got_a, want_a), f"pair {rep}: the larger call differs from tide_rs"
         assert _same(got_b, want_b), f"pair {rep}: the smaller call differs from tide_rs"
+
+
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")   # the refused capture
+def test_noalloc_captured_with_a_new_pointer_set(orc):
+    """A pointer set tide_rs has never uploaded, captured into a HIP graph
+    through tide_rs_noalloc for every rank (default and small footprint) and
+    replayed three times, with the program's own eager work between the
+    replays; every replay equals the oracle."""
+    shapes = [(37, 5), (4100,), (3, 3), (9000,), (129, 33)]
+    N = 4
+    plan = tide.Plan(shapes, N)
+    S = plan.S
+    grads = workloads.random_grads_for_shapes(shapes, N, seed_base=61, device="cuda")
+    table = tide.grad_table(plan, grads)
+    out = torch.empty(N, S, dtype=torch.float32, device="cuda")
+    out_small = torch.empty(N, S, dtype=torch.float32, device="cuda")
+    # the first call on the device (it looks up the scratch address) runs
+    # eagerly, on another plan, before the capture
+    warm = tide.Plan([(5, 7)], 2)
+    warm_grads = workloads.random_grads_for_shapes([(5, 7)], 2, seed_base=3, device="cuda")
+    tide.rs_noalloc(warm, 0, tide.grad_table(warm, warm_grads),
+                    torch.empty(warm.S, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+
+    # tide_rs cannot take this pointer set inside a capture (its plan would
+    # have to upload it)
+    g0 = torch.cuda.CUDAGraph()
+    err = None
+    note("tide_rs: capture refused for a pointer set never uploaded")
+    with torch.cuda.graph(g0):
+        try:
+            tide.rs(plan, 0, table, out[0])
+        except tide.TideError as e:
+            err = e
+    assert err is not None and "capture" in str(err)
+    del g0
+
+    g = torch.cuda.CUDAGraph()
+    note("tide_rs_noalloc: capture, 5 params x 4 ranks, a pointer set never uploaded")
+    with torch.cuda.graph(g):
+        for R in range(N):
+            tide.rs_noalloc(plan, R, table, out[R])
+            tide.rs_noalloc(plan, R, table, out_small[R], small=True)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(17)
+    for rep in range(3):
+        for rank in grads:
+            for t in rank:
+                t.copy_(torch.from_numpy(rng.standard_normal(t.numel()).astype(np.float32))
+                        .to(torch.bfloat16).view(t.shape))
+        out.view(torch.int32).fill_(F32_SENTINEL)
+        out_small.view(torch.int32).fill_(F32_SENTINEL)
+        torch.cuda.synchronize()
+        note(f"tide_rs_noalloc: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for R in range(N):
+            want = expected_rs(orc, shapes, N, R, grads, plan)
+            assert same_f32(out[R].cpu().numpy(), want), (rep, R)
+            assert same_f32(out_small[R].cpu().numpy(), want), (rep, R, "small")
+    del g
