@@ -56,7 +56,36 @@ CASES = [
      {"small": True}),
     ("ragged 40 params, 20 ranks (2-rank batches)", _ragged_shapes(40, 11), 20, [0, 19], {}),
     ("tiny, 4 ranks", workloads.WORKLOADS["tiny"].shapes, 4, [0, 1, 2, 3], {}),
+    ("ragged 50 params, 8 ranks, fp16 grads, mean (x 1/8), persistent grid of 7",
+     _ragged_shapes(50, 13), 8, [0, 7], {"dtype": torch.float16, "avg": True,
+                                          "max_workgroups": 7}),
+    ("ragged 30 params, 3 ranks, fp32 grads", _ragged_shapes(30, 15), 3, [1],
+     {"dtype": torch.float32}),
+    ("ragged 30 params, 1 rank", _ragged_shapes(30, 17), 1, [0], {}),
+    ("ragged 30 params, 6 ranks, gradients 2 bytes off 16-byte alignment",
+     _ragged_shapes(30, 19), 6, [2, 5], {"misalign": True}),
 ]
+
+
+def _prepare(grads, dtype, misalign):
+    """The cases' gradient variants: another element type (converted from
+    the seeded bf16 values), or every tensor one element into a buffer of its
+    own, so no gradient pointer is 16-byte aligned."""
+    if dtype is not None:
+        grads = [[t.to(dtype) for t in rank] for rank in grads]
+    if misalign:
+        moved = []
+        for rank in grads:
+            row = []
+            for t in rank:
+                buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+                v = buf[1:].view(t.shape)
+                v.copy_(t)
+                assert v.data_ptr() % 16 != 0
+                row.append(v)
+            moved.append(row)
+        grads = moved
+    return grads
 
 
 def test_noalloc_matches_tide_rs_back_to_back(orc):
@@ -66,10 +95,11 @@ def test_noalloc_matches_tide_rs_back_to_back(orc):
     # tide_rs_noalloc call back to back on the current stream.
     for name, shapes, N, ranks, kw in CASES:
         grads = workloads.random_grads_for_shapes(shapes, N, seed_base=100 + N, device="cuda")
+        grads = _prepare(grads, kw.get("dtype"), kw.get("misalign", False))
         plan = tide.Plan(shapes, N)
         table = tide.grad_table(plan, grads)
         odt = torch.bfloat16 if kw.get("out_bf16") else torch.float32
-        opts = {k: v for k, v in kw.items() if k != "out_bf16"}
+        opts = {k: v for k, v in kw.items() if k not in ("out_bf16", "dtype", "misalign")}
         for R in ranks:
             want = _sentinel(plan.S, odt)
             got = _sentinel(plan.S, odt)
