@@ -614,20 +614,23 @@ def layout_conversion_leg(step, tokens=8192, reps=3):
     return res
 
 
-def fit_fixed_cost(p1, p2):
-    """t = t0 + B / r through two (bytes, microseconds) points: (t0 in us,
-    r in GB/s)."""
-    (b1, t1), (b2, t2) = p1, p2
-    r = (b2 - b1) / (t2 - t1) / 1e3
-    return t1 - b1 / (r * 1e3), r
+def fit_fixed_cost(*points):
+    """Least-squares line t = t0 + B / r through two or more (bytes,
+    microseconds) points: (t0 in us, r in GB/s)."""
+    n = len(points)
+    mb = sum(b for b, _ in points) / n
+    mt = sum(t for _, t in points) / n
+    slope = sum((b - mb) * (t - mt) for b, t in points) / sum((b - mb) ** 2 for b, _ in points)
+    return mt - slope * mb, 1.0 / slope / 1e3
 
 
-def fit_leg(w, repeats=(1, 4), reps=20, warmup=3):
+def fit_leg(w, repeats=(1, 2, 4), reps=40, warmup=3):
     """Per-launch fixed cost and in-kernel rate of tide_rs and tide_ag on the
     workload's shapes: each call is timed on a bucket of K copies of the
     layer (K in `repeats`, separate gradients and buffers for every copy, so
-    nothing is re-read from a cache), and t = t0 + B / r is fitted through
-    the two (B, t) points."""
+    nothing is re-read from a cache), and the least-squares line
+    t = t0 + B / r is fitted through the (B, t) points; the residuals show
+    how far the points are from one line."""
     res = {"workload": w.name, "repeats": list(repeats)}
     pts = {"tide_rs": [], "tide_ag": []}
     for K in repeats:
@@ -663,12 +666,14 @@ def fit_leg(w, repeats=(1, 4), reps=20, warmup=3):
         torch.cuda.empty_cache()
     for name, p in pts.items():
         (b1, t1) = p[0]
-        t0, r = fit_fixed_cost(p[0], p[-1])
+        t0, r = fit_fixed_cost(*p)
+        resid = [t - (t0 + b / (r * 1e3)) for b, t in p]
         res[name] = {"points_bytes_us": p, "fixed_us": t0, "in_kernel_GBps": r,
                      "in_kernel_pct_of_peak": 100.0 * r / HBM_PEAK_GBPS,
-                     "single_GBps": b1 / t1 / 1e3}
+                     "residuals_us": resid, "single_GBps": b1 / t1 / 1e3}
         log(f"fit: {name}: fixed cost {t0:.1f} us per launch, in-kernel {r:.0f} GB/s "
-            f"({100 * r / HBM_PEAK_GBPS:.1f}% of peak)")
+            f"({100 * r / HBM_PEAK_GBPS:.1f}% of peak), residuals "
+            f"{', '.join(f'{x:+.1f}' for x in resid)} us")
     return res
 
 

@@ -107,3 +107,10 @@ def test_fixed_cost_fit():
     # 10 us fixed plus 1 GB per 160 us (6.25 TB/s): two calls of 1 and 4 GB
     t0, r = bench.fit_fixed_cost((1e9, 170.0), (4e9, 650.0))
     assert abs(t0 - 10.0) < 1e-9 and abs(r - 6250.0) < 1e-6
+    # three points on that line, and three off it by +2, -4 and +2 us: zero
+    # mean and no correlation with the bytes, so the least-squares line is
+    # the same
+    t0, r = bench.fit_fixed_cost((1e9, 170.0), (2e9, 330.0), (4e9, 650.0))
+    assert abs(t0 - 10.0) < 1e-9 and abs(r - 6250.0) < 1e-6
+    t0, r = bench.fit_fixed_cost((1e9, 172.0), (2.5e9, 406.0), (4e9, 652.0))
+    assert abs(r - 6250.0) < 1e-6 and abs(t0 - (10.0 + 0.0)) < 1e-9
