@@ -54,8 +54,9 @@
  * Replacing a set waits (on the host) until the launches that read it have
  * finished, through one event per stream that read it (up to 16 streams per
  * cached set; a further stream takes over the entry of one whose reads have
- * finished), never through a device-wide synchronisation.  A call on another stream that hits a set whose upload may still
- * be in flight makes its stream wait for that upload.
+ * finished).  It synchronises the whole device only if recording such an
+ * event failed.  A call on another stream that hits a set whose upload may
+ * still be in flight makes its stream wait for that upload.
  *
  * Graph capture.  tide_rs, tide_ag, tide_pack and tide_rs_slots may be
  * captured into a HIP graph (stream capture) once the plan has been used on
