@@ -74,6 +74,23 @@ KERNEL_SRCS = [os.path.join(ROOT, "parameter_layout_collectives_amd", "csrc", f)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_llama31_70b_layer.json")
 
 
+# The pages' own figures (NVIDIA hardware, up to 64 GPUs), quoted in the
+# bench line as context, never as targets: TIDE article ("FSDP通信终局：TIDE零
+# 拷贝集合通信优化") §"FSDP2通信开销的根源" (layout conversion share; NCCL
+# reduce-scatter slowing a single-wave GEMM) and §"性能表现" (step time,
+# reduce-scatter SM time, peak memory).
+PAGES_CONTEXT = {
+    "source": "TIDE article, kongchang.com: sections on the roots of FSDP2's communication "
+              "cost and on performance; NVIDIA hardware at up to 64 GPUs; context, not targets",
+    "layout_conversion_pct_of_step_llama31_70b_8k_tokens": 6.4,
+    "nccl_reduce_scatter_single_wave_gemm_slowdown_pct_max": 69.0,
+    "step_time_reduction_vs_stock_fsdp2_pct_max": 27.1,
+    "step_time_reduction_vs_fsdp2_symmmem_pct_max": 6.0,
+    "reduce_scatter_sm_time_reduction_factor": [12.5, 14.5],
+    "peak_memory_reduction_vs_fsdp2_symmmem_gib_max": 4.7,
+}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -1396,6 +1413,7 @@ def main():
             if k in corun_res},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "pages_context": PAGES_CONTEXT,
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "kernel_source_sha256_16": kernel_source_hash(),
     }

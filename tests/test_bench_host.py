@@ -114,3 +114,12 @@ def test_fixed_cost_fit():
     assert abs(t0 - 10.0) < 1e-9 and abs(r - 6250.0) < 1e-6
     t0, r = bench.fit_fixed_cost((1e9, 172.0), (2.5e9, 406.0), (4e9, 652.0))
     assert abs(r - 6250.0) < 1e-6 and abs(t0 - (10.0 + 0.0)) < 1e-9
+
+
+def test_pages_figures_are_context_only():
+    # quoted beside the measurements, never used as a target or in vs_baseline
+    ctx = bench.PAGES_CONTEXT
+    assert ctx["layout_conversion_pct_of_step_llama31_70b_8k_tokens"] == 6.4
+    assert ctx["nccl_reduce_scatter_single_wave_gemm_slowdown_pct_max"] == 69.0
+    assert ctx["step_time_reduction_vs_stock_fsdp2_pct_max"] == 27.1
+    assert "context, not targets" in ctx["source"]
