@@ -28,6 +28,11 @@ def _run(exe, marker):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
                UBSAN_OPTIONS="print_stacktrace=1", OMP_NUM_THREADS="2")
     run = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
+    if run.returncode != 0 and "LeakSanitizer has encountered a fatal error" in run.stderr:
+        # the leak checker itself cannot run here (e.g. under ptrace): keep
+        # the address and undefined-behaviour checks
+        env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=0"
+        run = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
     assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-6000:])
     assert marker in run.stdout
     assert "runtime error" not in run.stderr and "ERROR: AddressSanitizer" not in run.stderr
